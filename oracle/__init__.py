@@ -1,0 +1,16 @@
+"""CPU reference for int8-KV GQA attention.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``; never by the library.
+"""
+
+from .core import (  # noqa: F401
+    attention,
+    default_scale,
+    dequantize,
+    kv_head_of,
+    merge_partials,
+    prompt,
+    split_partials,
+    verify,
+)

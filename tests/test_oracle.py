@@ -1,0 +1,75 @@
+"""The oracle against its pins (CPU only)."""
+
+import numpy as np
+import pytest
+
+import oracle
+import pins
+
+
+def _attn(q, pos, kc, ks, vc, vs, sm_scale=None):
+    return oracle.attention(q, pos, kc, ks, vc, vs, sm_scale)
+
+
+@pytest.mark.parametrize("check", pins.ATTENTION_CHECKS, ids=lambda f: f.__name__)
+def test_attention_pin(check):
+    check(_attn)
+
+
+@pytest.mark.parametrize(
+    "check",
+    [pins.check_merge_single, pins.check_merge_equal_m, pins.check_merge_base2,
+     pins.check_merge_empty],
+    ids=lambda f: f.__name__,
+)
+def test_merge_pin(check):
+    check(oracle.merge_partials)
+
+
+def test_split_invariance():
+    pins.check_split_invariance(_attn, oracle.split_partials, oracle.merge_partials)
+
+
+def test_verify_and_prompt_positions():
+    """verify() puts row r at ctx+r; prompt() puts query i at q_pos0+i."""
+    q, kc, ks, vc, vs = pins.random_case(40, 3, 4, 2, 64, 20)
+    a = oracle.verify(q, kc, ks, vc, vs, ctx_len=10)
+    b = oracle.attention(q, [10, 11, 12], kc, ks, vc, vs)
+    assert np.array_equal(a, b)
+    c = oracle.prompt(q.astype(np.float16), kc, ks, vc, vs, q_pos0=4)
+    d = oracle.attention(q.astype(np.float16), [4, 5, 6], kc, ks, vc, vs)
+    assert np.array_equal(c, d)
+
+
+def test_row_subset_matches_full():
+    q, kc, ks, vc, vs = pins.random_case(41, 6, 4, 1, 64, 30)
+    pos = [24, 25, 26, 27, 28, 29]
+    full = oracle.attention(q, pos, kc, ks, vc, vs)
+    sub = oracle.attention(q, pos, kc, ks, vc, vs, rows=[1, 4])
+    assert np.array_equal(sub, full[[1, 4]])
+
+
+def test_dequantize_exact():
+    r = np.random.default_rng(42)
+    codes = r.integers(-127, 128, size=(2, 3, 64)).astype(np.int8)
+    scales = r.uniform(1e-4, 10, size=(2, 3, 2)).astype(np.float16)
+    got = oracle.dequantize(codes, scales)
+    assert np.array_equal(got, pins.deq(codes, scales))
+
+
+def test_sm_scale_argument():
+    """An explicit sm_scale replaces 1/sqrt(hd) (two-key closed form, scale 0.3)."""
+    import math
+
+    hd = 32
+    q = np.zeros((1, 1, hd), dtype=np.float32)
+    q[0, 0, 0] = 2.0
+    kc = np.zeros((1, 2, hd), dtype=np.int8)
+    kc[0, 1, 0] = 10
+    ks = np.full((1, 2, 1), 0.5, dtype=np.float16)
+    vc = np.zeros((1, 2, hd), dtype=np.int8)
+    vc[0, 1] = 1
+    vs = np.ones((1, 2, 1), dtype=np.float16)
+    got = oracle.attention(q, [1], kc, ks, vc, vs, sm_scale=0.3)
+    D = 2.0 * 10 * 0.5 * 0.3
+    assert abs(got[0, 0, 0] - math.exp(D) / (1 + math.exp(D))) < 1e-15
