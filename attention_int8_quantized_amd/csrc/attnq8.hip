@@ -1,0 +1,296 @@
+// Host side of the attnq8 C ABI: argument validation, launch planning and
+// kernel launches on the caller's stream.  See include/attnq8.h for the
+// contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/attnq8.h"
+#include "attend_kernel.h"
+
+namespace {
+
+using namespace attnq8;
+
+constexpr int kMaxVectorsPerGroup = 128;  // 8 waves x 16 query vectors
+constexpr int kTargetCUs = 256;           // MI355X compute units
+constexpr double kLog2e = 1.4426950408889634;
+
+thread_local char g_last_path[192] = "none";
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool head_dim_ok(int hd) { return hd == 64 || hd == 128 || hd == 256; }
+
+// Per-device architecture check, cached (0 = unknown, 1 = gfx950, 2 = other).
+int device_status() {
+  static signed char cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTNQ8_EHIP;
+  if (dev < 0 || dev >= 64) return ATTNQ8_EUNSUPPORTED;
+  if (cache[dev] == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTNQ8_EHIP;
+    cache[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+  }
+  return cache[dev] == 1 ? ATTNQ8_OK : ATTNQ8_EUNSUPPORTED;
+}
+
+int launch_status() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? ATTNQ8_OK : ATTNQ8_EHIP;
+}
+
+int auto_rows_per_group(int G, int n_rows) {
+  int rg = kMaxVectorsPerGroup / G;
+  if (rg > n_rows) rg = n_rows;
+  if (rg < 1) rg = 1;
+  return rg;
+}
+
+// Rows per workgroup for the prompt path: about four waves of 16 vectors,
+// preferring a whole number of 16-vector tiles.
+int prompt_rows_per_group(int G, int n_queries) {
+  int best = 64 / G;
+  if (best < 1) best = 1;
+  for (int r = best; r >= 1; --r) {
+    if ((r * G) % 16 == 0) {
+      best = r;
+      break;
+    }
+  }
+  if (best > n_queries) best = n_queries;
+  return best;
+}
+
+int splits_for(int n_keys, int n_groups, int n_kv_heads) {
+  const int tiles = (n_keys + 31) / 32;
+  const int units = n_groups * n_kv_heads;
+  int s = (kTargetCUs + units - 1) / units;
+  if (s > tiles) s = tiles;
+  if (s < 1) s = 1;
+  return s;
+}
+
+using KernelFn = void (*)(AttendArgs);
+
+template <int HD, bool QF32, bool FINAL>
+KernelFn pick_nw(int nw) {
+  switch (nw) {
+    case 1: return attend_q8_kernel<HD, 1, QF32, FINAL>;
+    case 2: return attend_q8_kernel<HD, 2, QF32, FINAL>;
+    case 3: return attend_q8_kernel<HD, 3, QF32, FINAL>;
+    case 4: return attend_q8_kernel<HD, 4, QF32, FINAL>;
+    case 5: return attend_q8_kernel<HD, 5, QF32, FINAL>;
+    case 6: return attend_q8_kernel<HD, 6, QF32, FINAL>;
+    case 7: return attend_q8_kernel<HD, 7, QF32, FINAL>;
+    case 8: return attend_q8_kernel<HD, 8, QF32, FINAL>;
+    default: return nullptr;
+  }
+}
+
+template <bool FINAL>
+KernelFn pick_kernel(int hd, bool qf32, int nw) {
+  switch (hd) {
+    case 64: return qf32 ? pick_nw<64, true, FINAL>(nw) : pick_nw<64, false, FINAL>(nw);
+    case 128: return qf32 ? pick_nw<128, true, FINAL>(nw) : pick_nw<128, false, FINAL>(nw);
+    case 256: return qf32 ? pick_nw<256, true, FINAL>(nw) : pick_nw<256, false, FINAL>(nw);
+    default: return nullptr;
+  }
+}
+
+int check_kv(const void* q, int q_dtype, const int8_t* kc, const uint16_t* ks, const int8_t* vc,
+             const uint16_t* vs, int hq, int hkv, int hd, int kv_stride) {
+  if (!q || !kc || !ks || !vc || !vs) return ATTNQ8_EINVAL;
+  if (q_dtype != ATTNQ8_F32 && q_dtype != ATTNQ8_F16) return ATTNQ8_EINVAL;
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0) return ATTNQ8_EINVAL;
+  if (!head_dim_ok(hd)) return ATTNQ8_EUNSUPPORTED;
+  if (hq / hkv > kMaxVectorsPerGroup) return ATTNQ8_EUNSUPPORTED;
+  if (kv_stride <= 0) return ATTNQ8_EINVAL;
+  if ((long long)hkv * kv_stride * hd > (1LL << 40)) return ATTNQ8_EINVAL;
+  if (!aligned(q, 16) || !aligned(kc, 16) || !aligned(vc, 16)) return ATTNQ8_EALIGN;
+  if (!aligned(ks, 4) || !aligned(vs, 4)) return ATTNQ8_EALIGN;
+  return ATTNQ8_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attnq8_status_string(int status) {
+  switch (status) {
+    case ATTNQ8_OK: return "ok";
+    case ATTNQ8_EINVAL: return "invalid argument";
+    case ATTNQ8_EUNSUPPORTED: return "unsupported device or shape";
+    case ATTNQ8_EALIGN: return "misaligned pointer";
+    case ATTNQ8_EWORKSPACE: return "workspace too small";
+    case ATTNQ8_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* attnq8_last_path(void) { return g_last_path; }
+
+int attn_verify_q8_splits(int n_q_heads, int n_kv_heads, int head_dim, int ctx_len, int n_rows,
+                          int rows_per_group) {
+  if (n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads) return ATTNQ8_EINVAL;
+  if (!head_dim_ok(head_dim)) return ATTNQ8_EUNSUPPORTED;
+  if (ctx_len < 0 || n_rows < 1 || n_rows > 32) return ATTNQ8_EINVAL;
+  const int G = n_q_heads / n_kv_heads;
+  if (G > kMaxVectorsPerGroup) return ATTNQ8_EUNSUPPORTED;
+  const int rg = rows_per_group > 0 ? rows_per_group : auto_rows_per_group(G, n_rows);
+  if (rows_per_group < 0 || rg * G > kMaxVectorsPerGroup) return ATTNQ8_EINVAL;
+  const int groups = (n_rows + rg - 1) / rg;
+  return splits_for(ctx_len + n_rows, groups, n_kv_heads);
+}
+
+size_t attn_verify_q8_workspace_bytes(int n_rows, int n_q_heads, int head_dim, int n_splits) {
+  if (n_rows <= 0 || n_q_heads <= 0 || head_dim <= 0 || n_splits <= 0) return 0;
+  return (size_t)n_splits * n_rows * n_q_heads * (size_t)(head_dim + 2) * sizeof(float);
+}
+
+int attn_verify_q8(const void* q, int q_dtype, const int8_t* k_codes, const uint16_t* k_scales,
+                   const int8_t* v_codes, const uint16_t* v_scales, int n_q_heads, int n_kv_heads,
+                   int head_dim, int kv_stride, int ctx_len, int n_rows, int rows_per_group,
+                   int n_splits, void* workspace, size_t workspace_bytes, float sm_scale,
+                   void* stream) {
+  int st = check_kv(q, q_dtype, k_codes, k_scales, v_codes, v_scales, n_q_heads, n_kv_heads,
+                    head_dim, kv_stride);
+  if (st) return st;
+  if (ctx_len < 0 || n_rows < 1 || n_rows > 32) return ATTNQ8_EINVAL;
+  if ((long long)ctx_len + n_rows > kv_stride) return ATTNQ8_EINVAL;
+  if (rows_per_group < 0 || n_splits < 0) return ATTNQ8_EINVAL;
+  if (!(sm_scale >= 0.0f) || isinf(sm_scale)) return ATTNQ8_EINVAL;
+  const int G = n_q_heads / n_kv_heads;
+  const int rg = rows_per_group > 0 ? rows_per_group : auto_rows_per_group(G, n_rows);
+  if (rg * G > kMaxVectorsPerGroup) return ATTNQ8_EINVAL;
+  const int groups = (n_rows + rg - 1) / rg;
+  const int n_keys = ctx_len + n_rows;
+  const int tiles = (n_keys + 31) / 32;
+  const int S = n_splits > 0 ? n_splits : splits_for(n_keys, groups, n_kv_heads);
+  if (S > tiles || S > 65535) return ATTNQ8_EINVAL;
+  if (!workspace) return ATTNQ8_EINVAL;
+  if (!aligned(workspace, 16)) return ATTNQ8_EALIGN;
+  const size_t need = attn_verify_q8_workspace_bytes(n_rows, n_q_heads, head_dim, S);
+  if (workspace_bytes < need) return ATTNQ8_EWORKSPACE;
+
+  st = device_status();
+  if (st) return st;
+
+  const int nw = (rg * G + 15) / 16;
+  KernelFn fn = pick_kernel<false>(head_dim, q_dtype == ATTNQ8_F32, nw);
+  if (!fn) return ATTNQ8_EUNSUPPORTED;
+  AttendArgs a;
+  a.q = q;
+  a.kc = k_codes;
+  a.ks = k_scales;
+  a.vc = v_codes;
+  a.vs = v_scales;
+  a.part_o = (float*)workspace;
+  a.part_ml = (float2*)((char*)workspace + (size_t)S * n_rows * n_q_heads * head_dim * sizeof(float));
+  a.out = nullptr;
+  a.Hq = n_q_heads;
+  a.G = G;
+  a.kv_stride = kv_stride;
+  a.pos0 = ctx_len;
+  a.n_rows = n_rows;
+  a.rows_per_wg = rg;
+  a.n_splits = S;
+  const float scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)head_dim));
+  a.kmul = (float)((double)scale * kLog2e);
+  hipLaunchKernelGGL(fn, dim3(S, groups, n_kv_heads), dim3(64 * nw), 0, (hipStream_t)stream, a);
+  st = launch_status();
+  if (st) return st;
+  snprintf(g_last_path, sizeof(g_last_path),
+           "verify hd%d q%s waves%d rows_per_group%d groups%d splits%d kv_heads%d", head_dim,
+           q_dtype == ATTNQ8_F32 ? "f32" : "f16", nw, rg, groups, S, n_kv_heads);
+  return ATTNQ8_OK;
+}
+
+int attn_reduce_partials(const void* workspace, size_t workspace_bytes, int n_rows, int n_q_heads,
+                         int head_dim, int n_splits, float* out, void* stream) {
+  if (!workspace || !out) return ATTNQ8_EINVAL;
+  if (n_rows < 1 || n_q_heads < 1 || n_splits < 1 || n_splits > 65535) return ATTNQ8_EINVAL;
+  if (!head_dim_ok(head_dim)) return ATTNQ8_EUNSUPPORTED;
+  if (!aligned(workspace, 16) || !aligned(out, 16)) return ATTNQ8_EALIGN;
+  if (workspace_bytes < attn_verify_q8_workspace_bytes(n_rows, n_q_heads, head_dim, n_splits))
+    return ATTNQ8_EWORKSPACE;
+  int st = device_status();
+  if (st) return st;
+  const int pairs = n_rows * n_q_heads;
+  const float* po = (const float*)workspace;
+  const float2* pml =
+      (const float2*)((const char*)workspace + (size_t)n_splits * pairs * head_dim * sizeof(float));
+  dim3 grid((pairs + 3) / 4), block(256);
+  hipStream_t s = (hipStream_t)stream;
+  switch (head_dim) {
+    case 64: hipLaunchKernelGGL(reduce_partials_kernel<64>, grid, block, 0, s, po, pml, n_splits, pairs, out); break;
+    case 128: hipLaunchKernelGGL(reduce_partials_kernel<128>, grid, block, 0, s, po, pml, n_splits, pairs, out); break;
+    default: hipLaunchKernelGGL(reduce_partials_kernel<256>, grid, block, 0, s, po, pml, n_splits, pairs, out); break;
+  }
+  st = launch_status();
+  if (st) return st;
+  snprintf(g_last_path, sizeof(g_last_path), "reduce hd%d pairs%d splits%d", head_dim, pairs, n_splits);
+  return ATTNQ8_OK;
+}
+
+int attn_prompt_q8(const void* q, int q_dtype, const int8_t* k_codes, const uint16_t* k_scales,
+                   const int8_t* v_codes, const uint16_t* v_scales, int n_q_heads, int n_kv_heads,
+                   int head_dim, int kv_stride, int kv_len, int q_pos0, int n_queries,
+                   float sm_scale, float* out, void* stream) {
+  int st = check_kv(q, q_dtype, k_codes, k_scales, v_codes, v_scales, n_q_heads, n_kv_heads,
+                    head_dim, kv_stride);
+  if (st) return st;
+  if (!out) return ATTNQ8_EINVAL;
+  if (!aligned(out, 16)) return ATTNQ8_EALIGN;
+  if (n_queries < 1 || q_pos0 < 0 || kv_len < 1) return ATTNQ8_EINVAL;
+  if ((long long)q_pos0 + n_queries > kv_len || kv_len > kv_stride) return ATTNQ8_EINVAL;
+  if (!(sm_scale >= 0.0f) || isinf(sm_scale)) return ATTNQ8_EINVAL;
+  const int G = n_q_heads / n_kv_heads;
+  const int rg = prompt_rows_per_group(G, n_queries);
+  const int groups = (n_queries + rg - 1) / rg;
+  if (groups > 65535) return ATTNQ8_EINVAL;
+  st = device_status();
+  if (st) return st;
+  const int nw = (rg * G + 15) / 16;
+  KernelFn fn = pick_kernel<true>(head_dim, q_dtype == ATTNQ8_F32, nw);
+  if (!fn) return ATTNQ8_EUNSUPPORTED;
+  AttendArgs a;
+  a.q = q;
+  a.kc = k_codes;
+  a.ks = k_scales;
+  a.vc = v_codes;
+  a.vs = v_scales;
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
+  a.out = out;
+  a.Hq = n_q_heads;
+  a.G = G;
+  a.kv_stride = kv_stride;
+  a.pos0 = q_pos0;
+  a.n_rows = n_queries;
+  a.rows_per_wg = rg;
+  a.n_splits = 1;
+  const float scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)head_dim));
+  a.kmul = (float)((double)scale * kLog2e);
+  hipLaunchKernelGGL(fn, dim3(1, groups, n_kv_heads), dim3(64 * nw), 0, (hipStream_t)stream, a);
+  st = launch_status();
+  if (st) return st;
+  snprintf(g_last_path, sizeof(g_last_path),
+           "prompt hd%d q%s waves%d rows_per_group%d groups%d kv_heads%d", head_dim,
+           q_dtype == ATTNQ8_F32 ? "f32" : "f16", nw, rg, groups, n_kv_heads);
+  return ATTNQ8_OK;
+}
+
+int attnq8_selftest_i8_to_f16(uint16_t* out, void* stream) {
+  if (!out) return ATTNQ8_EINVAL;
+  if (!aligned(out, 4)) return ATTNQ8_EALIGN;
+  int st = device_status();
+  if (st) return st;
+  hipLaunchKernelGGL(selftest_i8_to_f16_kernel, dim3(256), dim3(256), 0, (hipStream_t)stream, out);
+  return launch_status();
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+"""torch-facing wrappers over the attnq8 C ABI.
+
+Argument marshalling only: every step of the attention runs in the HIP
+kernels of libattnq8.so.  torch supplies device memory and the current HIP
+stream; tensors must already live on the GPU in the layouts of
+include/attnq8.h.
+"""
+
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+_QTYPES = {torch.float32: _lib.F32, torch.float16: _lib.F16}
+
+
+def _ptr(t: torch.Tensor) -> int:
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check_cache(q, k_codes, k_scales, v_codes, v_scales):
+    for name, t in (("q", q), ("k_codes", k_codes), ("k_scales", k_scales), ("v_codes", v_codes),
+                    ("v_scales", v_scales)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dtype not in _QTYPES:
+        raise ValueError("q must be float32 or float16")
+    if k_codes.dtype != torch.int8 or v_codes.dtype != torch.int8:
+        raise ValueError("codes must be int8")
+    if k_scales.dtype != torch.float16 or v_scales.dtype != torch.float16:
+        raise ValueError("scales must be float16")
+    if q.dim() != 3 or k_codes.dim() != 3 or k_scales.dim() != 3:
+        raise ValueError("q [rows][Hq][hd], codes [Hkv][stride][hd], scales [Hkv][stride][hd/32]")
+    if k_codes.shape != v_codes.shape or k_scales.shape != v_scales.shape:
+        raise ValueError("K and V caches must have the same shape")
+    hkv, stride, hd = k_codes.shape
+    if q.shape[2] != hd or k_scales.shape != (hkv, stride, hd // 32):
+        raise ValueError("inconsistent head_dim / scale shapes")
+    return q.shape[0], q.shape[1], hkv, hd, stride
+
+
+def verify_splits(n_q_heads, n_kv_heads, head_dim, ctx_len, n_rows, rows_per_group=0) -> int:
+    s = _lib.load().attn_verify_q8_splits(n_q_heads, n_kv_heads, head_dim, ctx_len, n_rows,
+                                          rows_per_group)
+    if s < 0:
+        raise _lib.Attnq8Error("attn_verify_q8_splits", s)
+    return s
+
+
+def workspace_bytes(n_rows, n_q_heads, head_dim, n_splits) -> int:
+    return int(_lib.load().attn_verify_q8_workspace_bytes(n_rows, n_q_heads, head_dim, n_splits))
+
+
+def verify_partials(q, k_codes, k_scales, v_codes, v_scales, ctx_len: int, rows_per_group: int = 0,
+                    n_splits: int = 0, sm_scale: float = 0.0,
+                    workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, int]:
+    """Run attn_verify_q8; returns (workspace uint8 tensor, n_splits)."""
+    n_rows, hq, hkv, hd, stride = _check_cache(q, k_codes, k_scales, v_codes, v_scales)
+    lib = _lib.load()
+    S = n_splits or verify_splits(hq, hkv, hd, ctx_len, n_rows, rows_per_group)
+    need = workspace_bytes(n_rows, hq, hd, S)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = lib.attn_verify_q8(_ptr(q), _QTYPES[q.dtype], _ptr(k_codes), _ptr(k_scales),
+                            _ptr(v_codes), _ptr(v_scales), hq, hkv, hd, stride, ctx_len, n_rows,
+                            rows_per_group, S, _ptr(workspace), workspace.numel(),
+                            float(sm_scale), _stream())
+    _lib.check("attn_verify_q8", st)
+    return workspace, S
+
+
+def split_views(workspace: torch.Tensor, n_splits, n_rows, n_q_heads, head_dim):
+    """(o [S][rows][Hq][hd], ml [S][rows][Hq][2]) float32 views of a workspace."""
+    n_o = n_splits * n_rows * n_q_heads * head_dim
+    f = workspace.view(torch.float32)
+    o = f[:n_o].view(n_splits, n_rows, n_q_heads, head_dim)
+    ml = f[n_o:n_o + 2 * n_splits * n_rows * n_q_heads].view(n_splits, n_rows, n_q_heads, 2)
+    return o, ml
+
+
+def reduce_partials(workspace: torch.Tensor, n_rows: int, n_q_heads: int, head_dim: int,
+                    n_splits: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty((n_rows, n_q_heads, head_dim), dtype=torch.float32,
+                          device=workspace.device)
+    st = _lib.load().attn_reduce_partials(_ptr(workspace), workspace.numel(), n_rows, n_q_heads,
+                                          head_dim, n_splits, _ptr(out), _stream())
+    _lib.check("attn_reduce_partials", st)
+    return out
+
+
+def verify(q, k_codes, k_scales, v_codes, v_scales, ctx_len: int, rows_per_group: int = 0,
+           n_splits: int = 0, sm_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+           workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Verify attention: attn_verify_q8 followed by attn_reduce_partials."""
+    ws, S = verify_partials(q, k_codes, k_scales, v_codes, v_scales, ctx_len, rows_per_group,
+                            n_splits, sm_scale, workspace)
+    return reduce_partials(ws, q.shape[0], q.shape[1], q.shape[2], S, out)
+
+
+def prompt(q, k_codes, k_scales, v_codes, v_scales, q_pos0: int, kv_len: Optional[int] = None,
+           sm_scale: float = 0.0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal prompt attention of q [n_queries][Hq][hd] at positions q_pos0 + i."""
+    n, hq, hkv, hd, stride = _check_cache(q, k_codes, k_scales, v_codes, v_scales)
+    if kv_len is None:
+        kv_len = q_pos0 + n
+    if out is None:
+        out = torch.empty((n, hq, hd), dtype=torch.float32, device=q.device)
+    st = _lib.load().attn_prompt_q8(_ptr(q), _QTYPES[q.dtype], _ptr(k_codes), _ptr(k_scales),
+                                    _ptr(v_codes), _ptr(v_scales), hq, hkv, hd, stride, kv_len,
+                                    q_pos0, n, float(sm_scale), _ptr(out), _stream())
+    _lib.check("attn_prompt_q8", st)
+    return out
+
+
+def selftest_i8_to_f16(device="cuda") -> torch.Tensor:
+    out = torch.empty(2 * 65536, dtype=torch.int16, device=device)
+    _lib.check("attnq8_selftest_i8_to_f16",
+               _lib.load().attnq8_selftest_i8_to_f16(_ptr(out), _stream()))
+    return out
+
+
+def last_path() -> str:
+    return _lib.last_path()

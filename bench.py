@@ -1,0 +1,264 @@
+"""Benchmark of the int8-KV attention hot path on one MI355X.
+
+One step = one verify call (attn_verify_q8 + attn_reduce_partials) on the
+verify-window workload (24 Q / 4 KV heads, head_dim 256, context 20,676, 8
+sequential rows) followed by one prompt call (attn_prompt_q8) on the prompt
+chunk (12 Q / 1 KV head, head_dim 256, 32,768-token int8 context, 2,048 causal
+queries).  Inputs are seeded synthetic data resident in HBM before timing, in
+several rotating copies so that the 256 MB Infinity Cache cannot serve
+repeats.  Kernel durations come from HIP events recorded on the library's
+stream around each launch; the GPU is held by a spin kernel while the timed
+launches are queued so that host submission latency does not enter them.
+
+Prints one JSON line (rank 0, N=1).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+FP16_MFMA_PEAK_TFLOPS = 2500.0
+METRIC = "verify-attn KV GB/s (% HBM peak); prompt-attn TFLOP/s (% MFMA peak)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--verify-workload", default="verify_window")
+    ap.add_argument("--prompt-workload", default="prompt_chunk")
+    ap.add_argument("--no-prompt", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rows-per-group", type=int, default=0)
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--rotate-bytes", type=float, default=1.1e9)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads as W
+    from attention_int8_quantized_amd import ops
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wv = W.WORKLOADS[args.verify_workload]
+    wp = W.WORKLOADS[args.prompt_workload]
+
+    # ---------------- inputs (host -> device, then device-side copies) ----------
+    log(f"generating {wv.name}")
+    iv = W.generate(wv)
+    v_host = [iv.q, iv.k_codes, iv.k_scales, iv.v_codes, iv.v_scales]
+    kv_bytes_v = sum(x.nbytes for x in v_host[1:])
+    nv = max(1, min(64, int(args.rotate_bytes // max(kv_bytes_v, 1)) + 1))
+    base = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in v_host]
+    vbufs = [base] + [[t.clone() for t in base] for _ in range(nv - 1)]
+    S = args.splits or ops.verify_splits(wv.n_q_heads, wv.n_kv_heads, wv.head_dim, wv.ctx_len,
+                                         wv.n_rows, args.rows_per_group)
+    ws = torch.empty(ops.workspace_bytes(wv.n_rows, wv.n_q_heads, wv.head_dim, S), dtype=torch.uint8,
+                     device=dev)
+    vout = torch.empty((wv.n_rows, wv.n_q_heads, wv.head_dim), dtype=torch.float32, device=dev)
+
+    pbufs = []
+    if not args.no_prompt:
+        log(f"generating {wp.name}")
+        ip = W.generate(wp)
+        p_host = [ip.q, ip.k_codes, ip.k_scales, ip.v_codes, ip.v_scales]
+        pbytes = sum(x.nbytes for x in p_host)
+        npb = max(1, min(16, int(0.35e9 // pbytes) + 1))
+        pbase = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in p_host]
+        pbufs = [pbase] + [[t.clone() for t in pbase] for _ in range(npb - 1)]
+        pout = torch.empty((wp.n_queries, wp.n_q_heads, wp.head_dim), dtype=torch.float32,
+                           device=dev)
+    torch.cuda.synchronize()
+
+    def verify_call(i):
+        q, kc, ks, vc, vs = vbufs[i % len(vbufs)]
+        ops.verify_partials(q, kc, ks, vc, vs, ctx_len=wv.ctx_len,
+                            rows_per_group=args.rows_per_group, n_splits=S, workspace=ws)
+
+    def reduce_call():
+        ops.reduce_partials(ws, wv.n_rows, wv.n_q_heads, wv.head_dim, S, out=vout)
+
+    def prompt_call(i):
+        q, kc, ks, vc, vs = pbufs[i % len(pbufs)]
+        ops.prompt(q, kc, ks, vc, vs, q_pos0=wp.pos0, kv_len=wp.kv_len, out=pout)
+
+    # ---------------- warmup -----------------------------------------------------
+    for i in range(args.warmup):
+        verify_call(i)
+        reduce_call()
+        if pbufs:
+            prompt_call(i)
+    torch.cuda.synchronize()
+    verify_path = None
+    verify_call(0)
+    verify_path = ops.last_path()
+    prompt_path = None
+    if pbufs:
+        prompt_call(0)
+        prompt_path = ops.last_path()
+    torch.cuda.synchronize()
+
+    # ---------------- timed region ------------------------------------------------
+    K = args.steps
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ev = [[E() for _ in range(4)] for _ in range(K)]
+    t_start, t_end = E(), E()
+    torch.cuda.synchronize()
+    # hold the GPU while the launches are queued (~40 us of host time per step)
+    torch.cuda._sleep(int(2.4e9 * (0.05e-3 * K + 0.02) / 1.0))
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(K):
+        e = ev[i]
+        e[0].record()
+        verify_call(i + 1)
+        e[1].record()
+        reduce_call()
+        e[2].record()
+        if pbufs:
+            prompt_call(i + 1)
+        e[3].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    k1 = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]) * 1e-3  # s
+    k2 = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]) * 1e-3
+    kp = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)]) * 1e-3
+    step_ms = t_start.elapsed_time(t_end) / K
+
+    vbytes = wv.visible_kv_bytes(args.rows_per_group or None) if wv.kind == "verify" else 0
+    unique = wv.unique_kv_bytes()
+    verify_s = float(np.mean(k1 + k2))
+    gbs = vbytes / verify_s / 1e9
+    k1_mean = float(np.mean(k1))
+    k1_gbs = vbytes / k1_mean / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8-kv/fp16-mfma/fp32-softmax",
+        "data": "synthetic (seeded N(0,1), int8 block-32 quantised KV)",
+        "config": {
+            "workload": wv.name,
+            "verify": {**W.describe(wv), "splits": S, "rotating_copies": len(vbufs),
+                       "path": verify_path},
+            "parallelism": "single-gpu",
+        },
+        "verify": {
+            "us_per_call": round(verify_s * 1e6, 3),
+            "kernel_us": round(k1_mean * 1e6, 3),
+            "reduce_us": round(float(np.mean(k2)) * 1e6, 3),
+            "kv_bytes": vbytes,
+            "unique_kv_bytes": unique,
+            "gbs": round(gbs, 2),
+            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+        },
+        "roofline": {
+            "kernel": "attend_q8_kernel (verify)",
+            "bound": "hbm",
+            "achieved": round(k1_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+        },
+    }
+    if pbufs:
+        flops = wp.algorithmic_flops()
+        kp_mean = float(np.mean(kp))
+        tf = flops / kp_mean / 1e12
+        res["prompt"] = {
+            "workload": wp.name,
+            "config": W.describe(wp),
+            "path": prompt_path,
+            "ms_per_call": round(kp_mean * 1e3, 4),
+            "tflops": round(tf, 2),
+            "frac_mfma": round(tf / FP16_MFMA_PEAK_TFLOPS, 4),
+            "rotating_copies": len(pbufs),
+        }
+        res["prompt_roofline"] = {
+            "kernel": "attend_q8_kernel (prompt)",
+            "bound": "mfma",
+            "achieved": round(tf, 2),
+            "peak": FP16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tf / FP16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": None,
+        }
+    res["host_wall_s"] = round(wall, 3)
+
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(wv, iv)
+
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(wv, iv):
+    """The fp64 oracle on the host, on a bounded sample of the verify workload."""
+    import oracle
+
+    try:
+        import threadpoolctl
+
+        info = threadpoolctl.threadpool_info()
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    # sample: all query vectors of the first KV head (a quarter of the work)
+    heads = list(range(wv.group))
+    q = iv.q[:, heads]
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.verify(q, iv.k_codes[:1], iv.k_scales[:1], iv.v_codes[:1], iv.v_scales[:1],
+                      wv.ctx_len)
+        reps += 1
+        if time.perf_counter() - t0 > 10.0 or reps >= 20:
+            break
+    dt = (time.perf_counter() - t0) / reps
+    sample_bytes = wv.visible_kv_bytes() / wv.n_kv_heads
+    return {
+        "value": round(sample_bytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{wv.name}: KV head 0 and its {wv.group} Q heads x {wv.n_rows} rows, "
+                  f"{reps} repetitions, {dt:.3f} s each",
+    }
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,153 @@
+/*
+ * attnq8 -- scaled-dot-product GQA attention over an int8 block-32 KV cache,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Two shapes of the same operation:
+ *
+ *  - the speculative-decode verifier: a run of sequential query rows after a
+ *    context; each workgroup owns every query vector of a row group that reads
+ *    one KV head and shares each K/V scan across them, writing split-context
+ *    partials that a reducer merges ("perf(gfx1100): share Q8 KV scans across
+ *    verifier rows", Summary);
+ *  - chunked causal prompt attention over a long int8 context with online
+ *    softmax and the V scale folded into the probabilities ("hip: gfx12 (RDNA4)
+ *    WMMA kernel for the int8-KV QSA prompt attention", What and How).
+ *
+ * Operation (both shapes).  For query row r at position pos_r, Q head h and
+ * KV head g = h / (n_q_heads / n_kv_heads):
+ *     Khat[t][j] = f32(k_scales[g][t][j/32]) * k_codes[g][t][j]   (same for V)
+ *     s_t = sm_scale * sum_j q[r][h][j] * Khat[t][j],  t = 0 .. pos_r
+ *     out[r][h][:] = sum_t exp(s_t - max s) Vhat[t][:] / sum_t exp(s_t - max s)
+ *
+ * Memory layouts (row-major, all buffers are DEVICE memory owned by the caller):
+ *     q          [n_rows][n_q_heads][head_dim]      fp32 or fp16 (q_dtype)
+ *     k_codes    [n_kv_heads][kv_stride][head_dim]  int8
+ *     k_scales   [n_kv_heads][kv_stride][head_dim/32] fp16 bit patterns
+ *     v_codes, v_scales: as K
+ *     out        [n_rows][n_q_heads][head_dim]      fp32
+ * A block is 32 consecutive head_dim elements of one (KV head, token) with one
+ * fp16 scale.  head_dim is 64, 128 or 256.
+ *
+ * Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream),
+ * never synchronise, never allocate device memory and keep no device state, so
+ * they may be captured into a HIP graph.  Every argument check runs on the host
+ * before anything is launched; on failure nothing is launched and a negative
+ * status is returned.  A device fault surfaces at the caller's next
+ * synchronisation, as for any HIP launch.  There is one code path per call: no
+ * fallback kernels.
+ */
+#ifndef ATTNQ8_H
+#define ATTNQ8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  ATTNQ8_OK = 0,
+  ATTNQ8_EINVAL = -1,      /* a size, count or pointer argument is out of range or NULL */
+  ATTNQ8_EUNSUPPORTED = -2,/* the current device is not gfx950, or the shape is not served */
+  ATTNQ8_EALIGN = -3,      /* a pointer is not aligned as documented */
+  ATTNQ8_EWORKSPACE = -4,  /* workspace smaller than attn_verify_q8_workspace_bytes() */
+  ATTNQ8_EHIP = -5         /* the HIP runtime reported an error while launching */
+};
+
+enum { ATTNQ8_F32 = 0, ATTNQ8_F16 = 1 };
+
+/* ---------------------------------------------------------------------------
+ * Verify attention ("perf(gfx1100): share Q8 KV scans across verifier rows",
+ * Summary and Kernel evidence).
+ *
+ * Row i of the n_rows query rows sits at position ctx_len + i and sees keys
+ * 0 .. ctx_len + i (the cache already holds the rows' own keys).  Rows are
+ * taken rows_per_group at a time; one workgroup holds every (row, Q head) of a
+ * group that reads one KV head -- rows_per_group * n_q_heads / n_kv_heads
+ * query vectors, at most 128 -- and splits the group's visible context into
+ * n_splits ranges of whole 32-key tiles.  rows_per_group = 0 picks the largest
+ * group that fits; n_splits = 0 picks attn_verify_q8_splits().  The grouping
+ * and split count change only the rounding of the result.
+ *
+ * Output: split-context partials in `workspace`, merged by
+ * attn_reduce_partials().  Workspace layout (fp32, 16-byte aligned):
+ *     o  [n_splits][n_rows][n_q_heads][head_dim]
+ *     ml [n_splits][n_rows][n_q_heads][2]          (m, l), after o
+ * With x_t = s_t * log2(e) (base-2 units), a split's partial over the keys it
+ * covers that the row sees is   l = sum 2^(x_t - m),  o = sum 2^(x_t - m) Vhat_t
+ * for a reference m near the largest x_t (not necessarily equal to it); a
+ * split with no visible key holds m = -inf, l = 0, o = 0.
+ *
+ * Requirements: n_q_heads % n_kv_heads == 0; 1 <= n_rows <= 32;
+ * ctx_len >= 0; ctx_len + n_rows <= kv_stride; q, codes and workspace 16-byte
+ * aligned, scales 4-byte aligned; workspace_bytes >=
+ * attn_verify_q8_workspace_bytes(n_rows, n_q_heads, head_dim, n_splits after
+ * auto selection).  sm_scale = 0 means 1/sqrt(head_dim).
+ * ------------------------------------------------------------------------- */
+int attn_verify_q8_splits(int n_q_heads, int n_kv_heads, int head_dim, int ctx_len,
+                          int n_rows, int rows_per_group);
+size_t attn_verify_q8_workspace_bytes(int n_rows, int n_q_heads, int head_dim,
+                                      int n_splits);
+int attn_verify_q8(const void* q, int q_dtype,
+                   const int8_t* k_codes, const uint16_t* k_scales,
+                   const int8_t* v_codes, const uint16_t* v_scales,
+                   int n_q_heads, int n_kv_heads, int head_dim,
+                   int kv_stride, int ctx_len, int n_rows,
+                   int rows_per_group, int n_splits,
+                   void* workspace, size_t workspace_bytes,
+                   float sm_scale, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Reducer: merge the partials of attn_verify_q8 ("partials layout and reducer",
+ * "perf(gfx1100): share Q8 KV scans across verifier rows", Summary):
+ *     M = max of m over splits with l > 0
+ *     out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
+ * in a fixed split order (run-to-run bitwise reproducible).  `workspace` holds
+ * the layout above for the given n_splits; out is fp32
+ * [n_rows][n_q_heads][head_dim], 16-byte aligned.  Every (row, head) must have
+ * at least one split with l > 0.
+ * ------------------------------------------------------------------------- */
+int attn_reduce_partials(const void* workspace, size_t workspace_bytes,
+                         int n_rows, int n_q_heads, int head_dim, int n_splits,
+                         float* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Prompt attention ("hip: gfx12 (RDNA4) WMMA kernel for the int8-KV QSA prompt
+ * attention", What, How and Measurements).
+ *
+ * Query i of the n_queries rows sits at position q_pos0 + i and sees keys
+ * 0 .. q_pos0 + i (causal).  Requirements: q_pos0 >= 0,
+ * q_pos0 + n_queries <= kv_len <= kv_stride, n_queries >= 1; q and out
+ * 16-byte aligned; codes 16-byte, scales 4-byte aligned.  Writes the
+ * normalised result to `out`.  sm_scale = 0 means 1/sqrt(head_dim).
+ * ------------------------------------------------------------------------- */
+int attn_prompt_q8(const void* q, int q_dtype,
+                   const int8_t* k_codes, const uint16_t* k_scales,
+                   const int8_t* v_codes, const uint16_t* v_scales,
+                   int n_q_heads, int n_kv_heads, int head_dim,
+                   int kv_stride, int kv_len, int q_pos0, int n_queries,
+                   float sm_scale, float* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Diagnostics.
+ *
+ * attnq8_selftest_i8_to_f16: run the device's int8 -> fp16 code conversion
+ * (exact, "hip: gfx12 (RDNA4) WMMA kernel for the int8-KV QSA prompt
+ * attention", How) over all 65,536 byte pairs: for p in [0, 65536), out[2p]
+ * and out[2p+1] receive the fp16 bit patterns of the signed bytes (p & 255)
+ * and (p >> 8).  out is a device buffer of 131,072 uint16 values.
+ *
+ * attnq8_status_string: a static description of a status code.
+ * attnq8_last_path: a static per-thread description of the kernel variant,
+ * grid and split count the calling thread's last successful call launched.
+ * ------------------------------------------------------------------------- */
+int attnq8_selftest_i8_to_f16(uint16_t* out, void* stream);
+const char* attnq8_status_string(int status);
+const char* attnq8_last_path(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTNQ8_H */

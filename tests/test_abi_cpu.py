@@ -1,0 +1,141 @@
+"""The C ABI library loads, exports every declared symbol and rejects bad
+arguments on the host before any HIP call (CPU only, no GPU needed)."""
+
+import ctypes
+import os
+
+import pytest
+
+from attention_int8_quantized_amd import _lib
+
+A = 0x10000  # a 16-byte aligned fake device address; never dereferenced here
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _lib.header_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib._SIGNATURES)
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4, -5):
+        assert _lib.status_string(st)
+    assert _lib.status_string(7) == "unknown status"
+
+
+def test_workspace_bytes(lib):
+    f = lib.attn_verify_q8_workspace_bytes
+    assert f(8, 24, 256, 64) == 64 * 8 * 24 * 258 * 4
+    assert f(0, 24, 256, 64) == 0
+    assert f(4, 4, 64, 0) == 0
+
+
+def test_auto_splits(lib):
+    f = lib.attn_verify_q8_splits
+    # 256 units of work over the CUs, never more splits than 32-key tiles
+    assert f(24, 4, 256, 20676, 8, 0) == 64
+    assert f(24, 4, 256, 131072, 4, 0) == 64
+    assert f(32, 8, 128, 8192, 32, 0) == 32
+    assert f(32, 8, 128, 8192, 32, 4) == 4
+    assert f(4, 1, 64, 256, 4, 0) == 9  # 260 keys -> 9 tiles
+    assert f(4, 1, 64, 0, 1, 0) == 1
+    assert f(4, 3, 64, 10, 4, 0) == _lib.EINVAL
+    assert f(4, 1, 96, 10, 4, 0) == _lib.EUNSUPPORTED
+    assert f(4, 1, 64, 10, 33, 0) == _lib.EINVAL
+    assert f(64, 1, 64, 10, 4, 4) == _lib.EINVAL  # 256 vectors per group > 128
+
+
+def _verify(lib, **kw):
+    args = dict(q=A, q_dtype=0, kc=A, ks=A, vc=A, vs=A, hq=4, hkv=1, hd=64, stride=300, ctx=256,
+                rows=4, rg=0, splits=0, ws=A, ws_bytes=1 << 30, sm=0.0, stream=None)
+    args.update(kw)
+    return lib.attn_verify_q8(args["q"], args["q_dtype"], args["kc"], args["ks"], args["vc"],
+                              args["vs"], args["hq"], args["hkv"], args["hd"], args["stride"],
+                              args["ctx"], args["rows"], args["rg"], args["splits"], args["ws"],
+                              args["ws_bytes"], args["sm"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), _lib.EINVAL),
+    (dict(kc=None), _lib.EINVAL),
+    (dict(vs=None), _lib.EINVAL),
+    (dict(ws=None), _lib.EINVAL),
+    (dict(q_dtype=2), _lib.EINVAL),
+    (dict(hkv=3), _lib.EINVAL),
+    (dict(hq=0), _lib.EINVAL),
+    (dict(hd=96), _lib.EUNSUPPORTED),
+    (dict(hd=512), _lib.EUNSUPPORTED),
+    (dict(rows=0), _lib.EINVAL),
+    (dict(rows=33), _lib.EINVAL),
+    (dict(ctx=-1), _lib.EINVAL),
+    (dict(ctx=297), _lib.EINVAL),          # ctx + rows > stride
+    (dict(rg=-1), _lib.EINVAL),
+    (dict(rg=40), _lib.EINVAL),            # 160 vectors per group
+    (dict(splits=10), _lib.EINVAL),        # more splits than 9 tiles
+    (dict(splits=-2), _lib.EINVAL),
+    (dict(sm=float("nan")), _lib.EINVAL),
+    (dict(sm=-1.0), _lib.EINVAL),
+    (dict(sm=float("inf")), _lib.EINVAL),
+    (dict(q=A + 8), _lib.EALIGN),
+    (dict(kc=A + 4), _lib.EALIGN),
+    (dict(ks=A + 2), _lib.EALIGN),
+    (dict(ws=A + 4), _lib.EALIGN),
+    (dict(ws_bytes=100), _lib.EWORKSPACE),
+    (dict(splits=9, ws_bytes=9 * 4 * 4 * 66 * 4 - 1), _lib.EWORKSPACE),
+])
+def test_verify_rejects_before_launch(lib, kw, status):
+    assert _verify(lib, **kw) == status
+
+
+def _prompt(lib, **kw):
+    args = dict(q=A, q_dtype=1, kc=A, ks=A, vc=A, vs=A, hq=12, hkv=1, hd=256, stride=4096,
+                kv_len=4096, pos0=2048, n=2048, sm=0.0, out=A, stream=None)
+    args.update(kw)
+    return lib.attn_prompt_q8(args["q"], args["q_dtype"], args["kc"], args["ks"], args["vc"],
+                              args["vs"], args["hq"], args["hkv"], args["hd"], args["stride"],
+                              args["kv_len"], args["pos0"], args["n"], args["sm"], args["out"],
+                              args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=None), _lib.EINVAL),
+    (dict(q=None), _lib.EINVAL),
+    (dict(n=0), _lib.EINVAL),
+    (dict(pos0=-1), _lib.EINVAL),
+    (dict(pos0=2049), _lib.EINVAL),        # last query beyond kv_len
+    (dict(kv_len=5000), _lib.EINVAL),      # kv_len > stride
+    (dict(hq=13, hkv=2), _lib.EINVAL),
+    (dict(hd=32), _lib.EUNSUPPORTED),
+    (dict(out=A + 4), _lib.EALIGN),
+    (dict(vc=A + 1), _lib.EALIGN),
+    (dict(sm=float("nan")), _lib.EINVAL),
+])
+def test_prompt_rejects_before_launch(lib, kw, status):
+    assert _prompt(lib, **kw) == status
+
+
+def test_reduce_rejects_before_launch(lib):
+    f = lib.attn_reduce_partials
+    assert f(None, 1 << 20, 4, 4, 64, 2, A, None) == _lib.EINVAL
+    assert f(A, 1 << 20, 4, 4, 64, 2, None, None) == _lib.EINVAL
+    assert f(A, 1 << 20, 0, 4, 64, 2, A, None) == _lib.EINVAL
+    assert f(A, 1 << 20, 4, 4, 64, 0, A, None) == _lib.EINVAL
+    assert f(A, 1 << 20, 4, 4, 48, 2, A, None) == _lib.EUNSUPPORTED
+    assert f(A + 4, 1 << 20, 4, 4, 64, 2, A, None) == _lib.EALIGN
+    assert f(A, 100, 4, 4, 64, 2, A, None) == _lib.EWORKSPACE
+
+
+def test_selftest_rejects_null(lib):
+    assert lib.attnq8_selftest_i8_to_f16(None, None) == _lib.EINVAL
+
+
+def test_library_is_in_tree():
+    assert os.path.dirname(_lib.LIB_PATH).endswith("attention_int8_quantized_amd")
+    assert isinstance(_lib.load(), ctypes.CDLL)
