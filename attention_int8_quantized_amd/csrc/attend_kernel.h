@@ -61,6 +61,125 @@ struct AttendArgs {
 constexpr float kRescaleSlack = 15.0f;
 constexpr float kRefBias = 8.0f;
 
+// One 32-key tile of K/V codes and scales, loaded with all of a thread's
+// loads in flight at once and then converted into the LDS operand layouts:
+//   Kf: K codes as fp16, A-operand fragments of S^T = K Q^T
+//       [block b][subtile u][lane][8]: key 16u + lane%16, dims 32b + 8(lane/16) + e
+//   Ks: K scale * sm_scale * log2(e), fp32 [block][key]
+//   Vf: V = dV * code as an exact fp16 hi/lo pair, A-operand fragments of
+//       O^T += V^T P^T: [dim tile d][hi|lo][lane][8]: dim 16d + lane%16, keys
+//       4(lane/16) + e for e < 4 and 16 + 4(lane/16) + e - 4 for e >= 4
+template <int HD, int NT>
+struct RawTile {
+  static constexpr int NB = HD / 32;
+  static constexpr int KCH = 2 * HD;             // 16-byte K code chunks per tile
+  static constexpr int CK = (KCH + NT - 1) / NT;
+  static constexpr int VT = 2 * HD;              // V tasks: 4 keys x 4 dims
+  static constexpr int CV = (VT + NT - 1) / NT;
+  static constexpr int KS = 32 * NB;             // K scales per tile
+  static constexpr int CS = (KS + NT - 1) / NT;
+
+  uint4 k[CK];
+  uint32_t v[CV][4];
+  uint16_t vs[CV][4];
+  uint16_t ks[CS];
+
+  __device__ __forceinline__ void load(const int8_t* kc, const uint16_t* ksc, const int8_t* vc,
+                                       const uint16_t* vsc, int key0, int k_end, int tid) {
+#pragma unroll
+    for (int i = 0; i < CK; ++i) {
+      const int f = tid + i * NT;
+      const int kk = f / (HD / 16);
+      const int c = f - kk * (HD / 16);
+      const int key = key0 + kk;
+      k[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (f < KCH && key < k_end) k[i] = *(const uint4*)(kc + (size_t)key * HD + 16 * c);
+    }
+#pragma unroll
+    for (int i = 0; i < CV; ++i) {
+      const int f = tid + i * NT;
+      const int c = f % (HD / 4);
+      const int q4 = f / (HD / 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = key0 + 4 * q4 + j;
+        v[i][j] = 0u;
+        vs[i][j] = 0;
+        if (f < VT && key < k_end) {
+          v[i][j] = *(const uint32_t*)(vc + (size_t)key * HD + 4 * c);
+          vs[i][j] = vsc[(size_t)key * NB + (c >> 3)];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CS; ++i) {
+      const int f = tid + i * NT;
+      const int kk = f / NB;
+      const int b = f - kk * NB;
+      const int key = key0 + kk;
+      ks[i] = 0;
+      if (f < KS && key < k_end) ks[i] = ksc[(size_t)key * NB + b];
+    }
+  }
+
+  __device__ __forceinline__ void stage(half_t* Kf, float* Ksm, half_t* Vf, float kmul,
+                                        int tid) const {
+#pragma unroll
+    for (int i = 0; i < CK; ++i) {
+      const int f = tid + i * NT;
+      if (f < KCH) {
+        const int kk = f / (HD / 16);
+        const int c = f - kk * (HD / 16);  // dims 16c .. 16c+15
+        const int b = c >> 1, hh = 2 * (c & 1), u = kk >> 4;
+        const half4_t x0 = dword_codes_to_f16(k[i].x);
+        const half4_t x1 = dword_codes_to_f16(k[i].y);
+        const half4_t x2 = dword_codes_to_f16(k[i].z);
+        const half4_t x3 = dword_codes_to_f16(k[i].w);
+        half_t* dst = &Kf[((b * 2 + u) * 64 + hh * 16 + (kk & 15)) * 8];
+        *(half8_t*)dst = (half8_t){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+        *(half8_t*)(dst + 16 * 8) = (half8_t){x2[0], x2[1], x2[2], x2[3], x3[0], x3[1], x3[2], x3[3]};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CS; ++i) {
+      const int f = tid + i * NT;
+      if (f < KS) {
+        const int kk = f / NB;
+        const int b = f - kk * NB;
+        Ksm[b * 32 + kk] = (float)f16_from_bits(ks[i]) * kmul;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CV; ++i) {
+      const int f = tid + i * NT;
+      if (f < VT) {
+        const int c = f % (HD / 4);   // dims 4c .. 4c+3
+        const int q4 = f / (HD / 4);  // keys 4 q4 .. 4 q4 + 3
+        const half2_t dv01 = {f16_from_bits(vs[i][0]), f16_from_bits(vs[i][1])};
+        const half2_t dv23 = {f16_from_bits(vs[i][2]), f16_from_bits(vs[i][3])};
+        const int u = q4 >> 2, hh = q4 & 3;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t sel = 0x0c000c00u | ((uint32_t)(4 + j) << 16) | (uint32_t)j;
+          const half2_t c01 = codes_to_f16(v[i][1], v[i][0], sel);
+          const half2_t c23 = codes_to_f16(v[i][3], v[i][2], sel);
+          const half2_t hi01 = c01 * dv01;
+          const half2_t hi23 = c23 * dv23;
+          const half2_t lo01 = __builtin_elementwise_fma(c01, dv01, -hi01);
+          const half2_t lo23 = __builtin_elementwise_fma(c23, dv23, -hi23);
+          const int D = 4 * c + j;
+          const int d = D >> 4;
+          const int ln = hh * 16 + (D & 15);
+          *(half4_t*)&Vf[((d * 2 + 0) * 64 + ln) * 8 + 4 * u] =
+              (half4_t){hi01[0], hi01[1], hi23[0], hi23[1]};
+          *(half4_t*)&Vf[((d * 2 + 1) * 64 + ln) * 8 + 4 * u] =
+              (half4_t){lo01[0], lo01[1], lo23[0], lo23[1]};
+        }
+      }
+    }
+  }
+};
+
 template <int HD, int NW, bool QF32, bool FINAL>
 __global__ __launch_bounds__(64 * NW) void attend_q8_kernel(const AttendArgs a) {
   constexpr int NB = HD / 32;   // 32-dim blocks (one scale each)
@@ -156,70 +275,21 @@ __global__ __launch_bounds__(64 * NW) void attend_q8_kernel(const AttendArgs a) 
   float l_part = 0.0f;
 
   const size_t head_rows = (size_t)g * a.kv_stride;
+  const int8_t* kc_head = a.kc + head_rows * HD;
+  const int8_t* vc_head = a.vc + head_rows * HD;
+  const uint16_t* ks_head = a.ks + head_rows * NB;
+  const uint16_t* vs_head = a.vs + head_rows * NB;
+
+  // Raw bytes of one 32-key tile held in registers: the next tile's loads are
+  // issued before the current tile is computed, so their latency overlaps it.
+  RawTile<HD, NT> raw;
+  if (t_begin < t_end) raw.load(kc_head, ks_head, vc_head, vs_head, t_begin * 32, k_end, tid);
 
   for (int t = t_begin; t < t_end; ++t) {
     const int key0 = t * 32;
-    __syncthreads();
-
-    // ---- staging: K codes -> fp16 fragments
-    for (int f = tid; f < NB * 2 * 64; f += NT) {
-      const int kk = f / (HD / 8);
-      const int c = f - kk * (HD / 8);  // 8-dim chunk: dims 8c .. 8c+7
-      const int key = key0 + kk;
-      uint2 w = {0u, 0u};
-      if (key < k_end) w = *(const uint2*)(a.kc + (head_rows + key) * HD + 8 * c);
-      const half4_t lo = dword_codes_to_f16(w.x);
-      const half4_t hi = dword_codes_to_f16(w.y);
-      const int b = c >> 2, hh = c & 3, u = kk >> 4;
-      const int ln = hh * 16 + (kk & 15);
-      *(half8_t*)&Kf[((b * 2 + u) * 64 + ln) * 8] =
-          (half8_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
-    // ---- staging: K scales * sm_scale * log2(e), fp32, [block][key]
-    for (int f = tid; f < NB * 32; f += NT) {
-      const int kk = f / NB;
-      const int b = f - kk * NB;
-      const int key = key0 + kk;
-      float s = 0.0f;
-      if (key < k_end) s = (float)f16_from_bits(a.ks[(head_rows + key) * NB + b]) * a.kmul;
-      Ks[b * 32 + kk] = s;
-    }
-    // ---- staging: V -> exact hi + lo fp16, V^T fragment order
-    for (int f = tid; f < 2 * HD; f += NT) {
-      const int c = f % (HD / 4);  // dims 4c .. 4c+3
-      const int q4 = f / (HD / 4); // keys 4*q4 .. 4*q4+3
-      const int kb = key0 + 4 * q4;
-      uint32_t w[4];
-      half_t dv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb + i;
-        w[i] = 0u;
-        dv[i] = (half_t)0.0f;
-        if (key < k_end) {
-          w[i] = *(const uint32_t*)(a.vc + (head_rows + key) * HD + 4 * c);
-          dv[i] = f16_from_bits(a.vs[(head_rows + key) * NB + (c >> 3)]);
-        }
-      }
-      const half2_t dv01 = {dv[0], dv[1]};
-      const half2_t dv23 = {dv[2], dv[3]};
-      const int u = q4 >> 2, hh = q4 & 3;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t sel = 0x0c000c00u | ((uint32_t)(4 + j) << 16) | (uint32_t)j;
-        const half2_t c01 = codes_to_f16(w[1], w[0], sel);
-        const half2_t c23 = codes_to_f16(w[3], w[2], sel);
-        const half2_t hi01 = c01 * dv01;
-        const half2_t hi23 = c23 * dv23;
-        const half2_t lo01 = __builtin_elementwise_fma(c01, dv01, -hi01);
-        const half2_t lo23 = __builtin_elementwise_fma(c23, dv23, -hi23);
-        const int D = 4 * c + j;
-        const int d = D >> 4;
-        const int ln = hh * 16 + (D & 15);
-        *(half4_t*)&Vf[((d * 2 + 0) * 64 + ln) * 8 + 4 * u] = (half4_t){hi01[0], hi01[1], hi23[0], hi23[1]};
-        *(half4_t*)&Vf[((d * 2 + 1) * 64 + ln) * 8 + 4 * u] = (half4_t){lo01[0], lo01[1], lo23[0], lo23[1]};
-      }
-    }
+    __syncthreads();  // every wave is done reading the previous tile
+    raw.stage(Kf, Ks, Vf, a.kmul, tid);
+    if (t + 1 < t_end) raw.load(kc_head, ks_head, vc_head, vs_head, key0 + 32, k_end, tid);
     __syncthreads();
 
     // ---- S^T = K Q^T for two 16-key subtiles
@@ -342,10 +412,16 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const float* __res
 // All 65,536 byte pairs through the code conversion used by the kernels.
 __global__ __launch_bounds__(256) void selftest_i8_to_f16_kernel(uint16_t* out) {
   const int p = blockIdx.x * 256 + threadIdx.x;  // 0 .. 65535
-  const uint32_t w = (uint32_t)p;                 // bytes: p & 255, p >> 8
+  uint32_t w = (uint32_t)p;                       // bytes: p & 255, p >> 8
+  // Make the word opaque to the optimiser, as a word loaded from memory is in
+  // the attention kernels; otherwise known-bits folding of the index rewrites
+  // the conversion and the test would not exercise the kernels' instructions.
+  asm volatile("" : "+v"(w));
   const half4_t h = dword_codes_to_f16(w);
-  out[2 * p + 0] = __builtin_bit_cast(uint16_t, h[0]);
-  out[2 * p + 1] = __builtin_bit_cast(uint16_t, h[1]);
+  // store the pair as one word (bit-casting vector elements one at a time is
+  // not reliable with this compiler)
+  const half2_t pair = {h[0], h[1]};
+  *(uint32_t*)(out + 2 * p) = __builtin_bit_cast(uint32_t, pair);
 }
 
 }  // namespace attnq8

@@ -30,8 +30,8 @@ __device__ __forceinline__ half2_t codes_to_f16(uint32_t src_hi, uint32_t src_lo
 
 // Four codes of one dword -> four fp16 values, in byte order.
 __device__ __forceinline__ half4_t dword_codes_to_f16(uint32_t w) {
-  const half2_t a = codes_to_f16(w, w, 0x0c010c00u);
-  const half2_t b = codes_to_f16(w, w, 0x0c030c02u);
+  const half2_t a = codes_to_f16(0u, w, 0x0c010c00u);
+  const half2_t b = codes_to_f16(0u, w, 0x0c030c02u);
   return (half4_t){a[0], a[1], b[0], b[1]};
 }
 

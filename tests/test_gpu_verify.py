@@ -104,7 +104,10 @@ def test_split_and_grouping_invariance():
         got = ops.verify(*dev, ctx_len=w.ctx_len, rows_per_group=rg, n_splits=s).cpu().numpy()
         e = np.abs(got - base).max() / scale
         note(f"  rows_per_group={rg} splits={s}: {e:.2e}")
-        assert e <= 1e-6
+        # Only the fp32 summation order changes: a sum over n ~ 3000 keys carries
+        # about sqrt(n) * 2^-24 ~ 3e-6 relative rounding, so two orders agree to
+        # a few 1e-6 of the output scale (well inside the 1e-5 oracle bound).
+        assert e <= 5e-6
 
 
 def test_causal_perturbation_leaves_earlier_rows():
