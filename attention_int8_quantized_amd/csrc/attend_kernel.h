@@ -1,30 +1,37 @@
-// The int8-KV attention tile kernel shared by the verify and prompt paths.
+// The int8-KV attention kernel shared by the verify and prompt paths.
 //
 // One workgroup owns the query vectors (row, Q head) of a group of consecutive
 // rows that read one KV head -- the "one owner of several query rows shares
 // every K/V scan" organisation of "perf(gfx1100): share Q8 KV scans across
 // verifier rows" (Summary) -- and scans one range of that head's keys, 32 keys
-// at a time:
+// per tile.  Each wave owns 16 query vectors.
 //
-//   1. cooperative staging: the workgroup reads the tile's int8 K/V codes and
-//      fp16 scales with coalesced loads, converts K codes exactly to fp16
-//      (fragment order), stores K scales * sm_scale * log2(e) as fp32, and
-//      dequantises V exactly into an fp16 hi + lo pair (V = dV * code has at
-//      most 18 significant bits; hi holds the rounded top 11, the fma residual
-//      the rest), transposed into the MFMA fragment order of V^T;
-//   2. per wave (16 query vectors): S^T = K Q^T on v_mfma_f32_16x16x32_f16, one
-//      32-dim block per MFMA (q is split hi + lo when given in fp32, after a
-//      per-vector power-of-two scaling that keeps both parts normal), each
-//      block's dot scaled by its K scale in fp32 in fixed block order;
-//   3. causal / range mask, online softmax in base 2 with a lazily moved
-//      reference point, p split into fp16 hi + lo;
-//   4. O^T += V^T P^T on the same MFMA as (Vhi,Phi) + (Vlo,Phi) + (Vhi,Plo).
+// Data movement: the int8 K/V codes and fp16 scales of a tile are copied from
+// HBM straight into LDS by direct-to-LDS buffer loads (no registers, no
+// conversion pass), into a ring of DEPTH tiles, so DEPTH-1 tiles are in flight
+// while one is computed; one workgroup barrier per tile.  Buffer ranges end at
+// the split's last key, so the ragged last tile reads zeros.
 //
-// The page's accuracy contract ("hip: gfx12 (RDNA4) WMMA kernel for the
-// int8-KV QSA prompt attention", How: fp16 hi+lo of q and p, fixed summation
-// order, online softmax, V scale folded into p) is kept in spirit: here the V
-// scale is folded into an exact hi+lo V tile instead of into p, which keeps the
-// fold exact for any scale magnitude.
+// Per wave and tile:
+//   S^T = K Q^T on v_mfma_f32_16x16x32_f16, one 32-dim block per MFMA: the K
+//     fragment is read from LDS with ds_read_b64 and converted exactly to
+//     fp16; q is held in registers, split hi + lo when given in fp32 after a
+//     per-vector power-of-two scaling that keeps both parts normal; each
+//     block's dot is scaled by its fp16 K scale in fp32, in fixed block order;
+//   causal / range mask, online softmax in base 2 with a lazily moved
+//     reference point, p split into fp16 hi + lo;
+//   O^T += V^T P^T on the same MFMA: the V^T fragment (8 keys of one dim per
+//     lane) comes from the natural-layout int8 tile through the gfx950
+//     transposing read ds_read_b64_tr_b8, is converted exactly and multiplied
+//     by its per-key V scale into an exact fp16 hi + lo pair (dV * code has at
+//     most 18 significant bits; hi is the rounded product, lo the fma
+//     residual), and O^T accumulates (Vhi,Phi) + (Vlo,Phi) + (Vhi,Plo).
+//
+// The accuracy contract of "hip: gfx12 (RDNA4) WMMA kernel for the int8-KV QSA
+// prompt attention" (How: fp16 hi+lo of q and p, fixed summation order, online
+// softmax, V scale folded into p) is kept in substance; the V scale is folded
+// into an exact hi+lo V fragment instead of into p, which keeps the fold exact
+// for any scale magnitude.
 //
 // The workgroup writes either split partials (m, l, o) or, when it covers every
 // key its rows see, the normalised output.
@@ -60,139 +67,99 @@ struct AttendArgs {
 // above fp16's subnormal range so that their hi + lo split keeps 22 bits.
 constexpr float kRescaleSlack = 15.0f;
 constexpr float kRefBias = 8.0f;
+constexpr int kRingDepth = 4;
 
-// One 32-key tile of K/V codes and scales, loaded with all of a thread's
-// loads in flight at once and then converted into the LDS operand layouts:
-//   Kf: K codes as fp16, A-operand fragments of S^T = K Q^T
-//       [block b][subtile u][lane][8]: key 16u + lane%16, dims 32b + 8(lane/16) + e
-//   Ks: K scale * sm_scale * log2(e), fp32 [block][key]
-//   Vf: V = dV * code as an exact fp16 hi/lo pair, A-operand fragments of
-//       O^T += V^T P^T: [dim tile d][hi|lo][lane][8]: dim 16d + lane%16, keys
-//       4(lane/16) + e for e < 4 and 16 + 4(lane/16) + e - 4 for e >= 4
-template <int HD, int NT>
-struct RawTile {
+// LDS layout of one 32-key ring stage (bytes):
+//   K codes  [32 keys][HD]  int8, 16-byte chunks of a row permuted by chunk_swizzle
+//   V codes  [32 keys][HD]  int8, same permutation
+//   K scales [32 keys][HD/32] fp16
+//   V scales [32 keys][HD/32] fp16
+template <int HD>
+struct Stage {
   static constexpr int NB = HD / 32;
-  static constexpr int KCH = 2 * HD;             // 16-byte K code chunks per tile
-  static constexpr int CK = (KCH + NT - 1) / NT;
-  static constexpr int VT = 2 * HD;              // V tasks: 4 keys x 4 dims
-  static constexpr int CV = (VT + NT - 1) / NT;
-  static constexpr int KS = 32 * NB;             // K scales per tile
-  static constexpr int CS = (KS + NT - 1) / NT;
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = 32 * HD;
+  static constexpr int KS_OFF = 64 * HD;
+  static constexpr int VS_OFF = 66 * HD;
+  static constexpr int BYTES = 68 * HD;
+  static constexpr int CODE_OPS = HD / 32;                  // 1 KB copies per code tile
+  static constexpr int SCALE_OPS = HD >= 128 ? HD / 128 : 1;  // 256 B copies per scale tile
+  static constexpr int NOPS = 2 * CODE_OPS + 2 * SCALE_OPS;
+  static constexpr int C = HD / 16;                         // 16-byte chunks per key row
+  static constexpr int R = 16 / C;                          // key rows per 256 bytes
+};
 
-  uint4 k[CK];
-  uint32_t v[CV][4];
-  uint16_t vs[CV][4];
-  uint16_t ks[CS];
+// Slot of 16-byte chunk `c` of tile row `key` (0..31).  Chosen so that the 16
+// rows read by one 16-lane group -- 16 consecutive keys for K fragments, keys
+// {4h..4h+3, 16+4h..16+4h+3} for the transposing V reads -- land in distinct
+// 16-byte bank groups.
+template <int HD>
+__device__ __forceinline__ int chunk_slot(int key, int c) {
+  constexpr int C = Stage<HD>::C, R = Stage<HD>::R;
+  return c ^ (((key / R) ^ ((key >> 4) * (C / 2))) & (C - 1));
+}
 
-  __device__ __forceinline__ void load(const int8_t* kc, const uint16_t* ksc, const int8_t* vc,
-                                       const uint16_t* vsc, int key0, int k_end, int tid) {
+template <int HD, int NW>
+struct TileCopier {
+  using L = Stage<HD>;
+  static constexpr int MAXC = (L::NOPS + NW - 1) / NW;  // copies per wave (max)
+  static constexpr int MINC = L::NOPS / NW;             // copies per wave (min)
+
+  __amdgpu_buffer_rsrc_t kc, vc, ks, vs;
+  int wave, lane;
+
+  // number of copies this wave issues per tile
+  __device__ __forceinline__ int count() const { return (L::NOPS - wave + NW - 1) / NW; }
+
+  // Copy tile starting at key0 into the stage at lds (or zeros when !live).
+  __device__ __forceinline__ void issue(uint32_t lds, int key0, bool live) const {
+    constexpr int kOut = 0x7ffffff0;  // past every buffer range: stores zeros
 #pragma unroll
-    for (int i = 0; i < CK; ++i) {
-      const int f = tid + i * NT;
-      const int kk = f / (HD / 16);
-      const int c = f - kk * (HD / 16);
-      const int key = key0 + kk;
-      k[i] = make_uint4(0u, 0u, 0u, 0u);
-      if (f < KCH && key < k_end) k[i] = *(const uint4*)(kc + (size_t)key * HD + 16 * c);
-    }
-#pragma unroll
-    for (int i = 0; i < CV; ++i) {
-      const int f = tid + i * NT;
-      const int c = f % (HD / 4);
-      const int q4 = f / (HD / 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = key0 + 4 * q4 + j;
-        v[i][j] = 0u;
-        vs[i][j] = 0;
-        if (f < VT && key < k_end) {
-          v[i][j] = *(const uint32_t*)(vc + (size_t)key * HD + 4 * c);
-          vs[i][j] = vsc[(size_t)key * NB + (c >> 3)];
+    for (int i = 0; i < MAXC; ++i) {
+      const int o = wave + i * NW;
+      if (o < L::NOPS) {
+        if (o < 2 * L::CODE_OPS) {
+          const bool is_v = o >= L::CODE_OPS;
+          const int j = is_v ? o - L::CODE_OPS : o;
+          const int pos = j * 1024 + 16 * lane;
+          const int row = pos / HD;
+          const int slot = (pos % HD) / 16;
+          const int c = chunk_slot<HD>(row, slot);  // the permutation is an involution
+          const int off = live ? (key0 + row) * HD + 16 * c : kOut;
+          dma_b128(is_v ? vc : kc, lds + (is_v ? L::V_OFF : L::K_OFF) + j * 1024, off);
+        } else {
+          const int j = o - 2 * L::CODE_OPS;
+          const bool is_v = j >= L::SCALE_OPS;
+          const int jj = is_v ? j - L::SCALE_OPS : j;
+          const int byte = jj * 256 + 4 * lane;
+          const int off = (live && byte < 2 * HD) ? key0 * 2 * L::NB + byte : kOut;
+          if (byte < 2 * HD)
+            dma_b32(is_v ? vs : ks, lds + (is_v ? L::VS_OFF : L::KS_OFF) + jj * 256, off);
         }
       }
-    }
-#pragma unroll
-    for (int i = 0; i < CS; ++i) {
-      const int f = tid + i * NT;
-      const int kk = f / NB;
-      const int b = f - kk * NB;
-      const int key = key0 + kk;
-      ks[i] = 0;
-      if (f < KS && key < k_end) ks[i] = ksc[(size_t)key * NB + b];
     }
   }
 
-  __device__ __forceinline__ void stage(half_t* Kf, float* Ksm, half_t* Vf, float kmul,
-                                        int tid) const {
-#pragma unroll
-    for (int i = 0; i < CK; ++i) {
-      const int f = tid + i * NT;
-      if (f < KCH) {
-        const int kk = f / (HD / 16);
-        const int c = f - kk * (HD / 16);  // dims 16c .. 16c+15
-        const int b = c >> 1, hh = 2 * (c & 1), u = kk >> 4;
-        const half4_t x0 = dword_codes_to_f16(k[i].x);
-        const half4_t x1 = dword_codes_to_f16(k[i].y);
-        const half4_t x2 = dword_codes_to_f16(k[i].z);
-        const half4_t x3 = dword_codes_to_f16(k[i].w);
-        half_t* dst = &Kf[((b * 2 + u) * 64 + hh * 16 + (kk & 15)) * 8];
-        *(half8_t*)dst = (half8_t){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-        *(half8_t*)(dst + 16 * 8) = (half8_t){x2[0], x2[1], x2[2], x2[3], x3[0], x3[1], x3[2], x3[3]};
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < CS; ++i) {
-      const int f = tid + i * NT;
-      if (f < KS) {
-        const int kk = f / NB;
-        const int b = f - kk * NB;
-        Ksm[b * 32 + kk] = (float)f16_from_bits(ks[i]) * kmul;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < CV; ++i) {
-      const int f = tid + i * NT;
-      if (f < VT) {
-        const int c = f % (HD / 4);   // dims 4c .. 4c+3
-        const int q4 = f / (HD / 4);  // keys 4 q4 .. 4 q4 + 3
-        const half2_t dv01 = {f16_from_bits(vs[i][0]), f16_from_bits(vs[i][1])};
-        const half2_t dv23 = {f16_from_bits(vs[i][2]), f16_from_bits(vs[i][3])};
-        const int u = q4 >> 2, hh = q4 & 3;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t sel = 0x0c000c00u | ((uint32_t)(4 + j) << 16) | (uint32_t)j;
-          const half2_t c01 = codes_to_f16(v[i][1], v[i][0], sel);
-          const half2_t c23 = codes_to_f16(v[i][3], v[i][2], sel);
-          const half2_t hi01 = c01 * dv01;
-          const half2_t hi23 = c23 * dv23;
-          const half2_t lo01 = __builtin_elementwise_fma(c01, dv01, -hi01);
-          const half2_t lo23 = __builtin_elementwise_fma(c23, dv23, -hi23);
-          const int D = 4 * c + j;
-          const int d = D >> 4;
-          const int ln = hh * 16 + (D & 15);
-          *(half4_t*)&Vf[((d * 2 + 0) * 64 + ln) * 8 + 4 * u] =
-              (half4_t){hi01[0], hi01[1], hi23[0], hi23[1]};
-          *(half4_t*)&Vf[((d * 2 + 1) * 64 + ln) * 8 + 4 * u] =
-              (half4_t){lo01[0], lo01[1], lo23[0], lo23[1]};
-        }
-      }
-    }
+  // Wait until this wave's copies of all but the newest `newer` tiles landed.
+  template <int newer>
+  __device__ __forceinline__ void wait_all_but() const {
+    if (count() == MAXC) wait_vmcnt<MAXC * newer>();
+    else wait_vmcnt<MINC * newer>();
   }
 };
 
 template <int HD, int NW, bool QF32, bool FINAL>
 __global__ __launch_bounds__(64 * NW) void attend_q8_kernel(const AttendArgs a) {
-  constexpr int NB = HD / 32;   // 32-dim blocks (one scale each)
-  constexpr int ND = HD / 16;   // 16-dim output tiles
-  constexpr int NT = 64 * NW;   // threads
+  using L = Stage<HD>;
+  constexpr int NB = L::NB;
+  constexpr int ND = HD / 16;  // 16-dim output tiles
+  constexpr int D = kRingDepth;
 
-  __shared__ __attribute__((aligned(16))) half_t Kf[NB * 2 * 64 * 8];
-  __shared__ __attribute__((aligned(16))) float Ks[NB * 32];
-  __shared__ __attribute__((aligned(16))) half_t Vf[ND * 2 * 64 * 8];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[D * L::BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int h4 = lane >> 4;
   const int n16 = lane & 15;
 
@@ -214,6 +181,20 @@ __global__ __launch_bounds__(64 * NW) void attend_q8_kernel(const AttendArgs a) 
   const int vr = v_ok ? v / a.G : 0;
   const int vh = v_ok ? g * a.G + (v - vr * a.G) : 0;
   const int lim = v_ok ? a.pos0 + r0 + vr : -1;  // last key this vector sees
+
+  // ---- start the copies first so that their latency overlaps the q setup
+  const size_t head_rows = (size_t)g * a.kv_stride;
+  TileCopier<HD, NW> cp;
+  cp.kc = make_rsrc(a.kc + head_rows * HD, k_end * HD);
+  cp.vc = make_rsrc(a.vc + head_rows * HD, k_end * HD);
+  cp.ks = make_rsrc(a.ks + head_rows * NB, k_end * NB * 2);
+  cp.vs = make_rsrc(a.vs + head_rows * NB, k_end * NB * 2);
+  cp.wave = wave;
+  cp.lane = lane;
+  const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
+#pragma unroll
+  for (int s = 0; s < D - 1; ++s)
+    cp.issue(ring0 + s * L::BYTES, (t_begin + s) * 32, t_begin + s < t_end);
 
   // ---- q fragments: B operand of S^T = K Q^T (lane: vector n16, dims 32b + 8*h4 + e)
   half8_t qhi[NB];
@@ -267,6 +248,14 @@ __global__ __launch_bounds__(64 * NW) void attend_q8_kernel(const AttendArgs a) 
       }
     }
   }
+  const float xmul = a.kmul * inv_qmul;  // exact: inv_qmul is a power of two
+
+  // per-lane LDS offsets that do not change from tile to tile
+  // K fragment rows: key 16u + n16; V transposing reads: lane 16h + 2k + s addresses
+  // key pi(h, k) = (k < 4 ? 4h + k : 16 + 4h + k - 4), dims 16d + 8s.
+  const int tk = (lane & 15) >> 1;
+  const int vkey = (tk < 4) ? 4 * h4 + tk : 16 + 4 * h4 + (tk - 4);
+  const int vsbit = lane & 1;
 
   float4_t O[ND];
 #pragma unroll
@@ -274,38 +263,41 @@ __global__ __launch_bounds__(64 * NW) void attend_q8_kernel(const AttendArgs a) 
   float m_ref = -INFINITY;
   float l_part = 0.0f;
 
-  const size_t head_rows = (size_t)g * a.kv_stride;
-  const int8_t* kc_head = a.kc + head_rows * HD;
-  const int8_t* vc_head = a.vc + head_rows * HD;
-  const uint16_t* ks_head = a.ks + head_rows * NB;
-  const uint16_t* vs_head = a.vs + head_rows * NB;
-
-  // Raw bytes of one 32-key tile held in registers: the next tile's loads are
-  // issued before the current tile is computed, so their latency overlaps it.
-  RawTile<HD, NT> raw;
-  if (t_begin < t_end) raw.load(kc_head, ks_head, vc_head, vs_head, t_begin * 32, k_end, tid);
-
+  int slot = 0;
   for (int t = t_begin; t < t_end; ++t) {
     const int key0 = t * 32;
-    __syncthreads();  // every wave is done reading the previous tile
-    raw.stage(Kf, Ks, Vf, a.kmul, tid);
-    if (t + 1 < t_end) raw.load(kc_head, ks_head, vc_head, vs_head, key0 + 32, k_end, tid);
-    __syncthreads();
+    cp.template wait_all_but<D - 2>();  // this wave's copies of tile t landed
+    __syncthreads();                    // everyone's landed; tile t-1 is free
+    cp.issue(ring0 + ((slot + D - 1) % D) * L::BYTES, key0 + (D - 1) * 32, t + D - 1 < t_end);
+
+    const uint8_t* st = ring + slot * L::BYTES;
+    const uint8_t* Kt = st + L::K_OFF;
+    const uint8_t* Vt = st + L::V_OFF;
+    const half_t* Kst = (const half_t*)(st + L::KS_OFF);
+    const half_t* Vst = (const half_t*)(st + L::VS_OFF);
 
     // ---- S^T = K Q^T for two 16-key subtiles
     float4_t s[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       s[u] = (float4_t){0, 0, 0, 0};
+      const int kk = 16 * u + n16;
+      half_t dk[4][NB];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) dk[e][b] = Kst[(16 * u + 4 * h4 + e) * NB + b];
+      }
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const half8_t ka = *(const half8_t*)&Kf[((b * 2 + u) * 64 + lane) * 8];
+        const int c = 2 * b + (h4 >> 1);
+        const uint2 w = *(const uint2*)(Kt + kk * HD + 16 * chunk_slot<HD>(kk, c) + 8 * (h4 & 1));
+        const half8_t ka = codes8_to_f16(w.x, w.y);
         float4_t acc = {0, 0, 0, 0};
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qhi[b], acc, 0, 0, 0);
         if (QF32) acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qlo[b], acc, 0, 0, 0);
-        const float4_t ksc = *(const float4_t*)&Ks[b * 32 + 16 * u + 4 * h4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s[u][e] = fmaf(ksc[e], acc[e], s[u][e]);
+        for (int e = 0; e < 4; ++e) s[u][e] = fmaf((float)dk[e][b], acc[e], s[u][e]);
       }
     }
 
@@ -318,7 +310,7 @@ __global__ __launch_bounds__(64 * NW) void attend_q8_kernel(const AttendArgs a) 
       for (int e = 0; e < 4; ++e) {
         const int key = key0 + 16 * u + 4 * h4 + e;
         const bool vis = (key < k_end) && (key <= lim);
-        x[u][e] = vis ? s[u][e] * inv_qmul : -INFINITY;
+        x[u][e] = vis ? s[u][e] * xmul : -INFINITY;
         tmax = fmaxf(tmax, x[u][e]);
       }
     }
@@ -347,15 +339,33 @@ __global__ __launch_bounds__(64 * NW) void attend_q8_kernel(const AttendArgs a) 
     }
 
     // ---- O^T += V^T P^T
+    // V scales of this lane group's keys pi(h4, e), e = 0..7
+    half_t dv[8][NB];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int key = (e < 4) ? 4 * h4 + e : 16 + 4 * h4 + (e - 4);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) dv[e][b] = Vst[key * NB + b];
+    }
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
-      const half8_t vh = *(const half8_t*)&Vf[((d * 2 + 0) * 64 + lane) * 8];
-      const half8_t vl = *(const half8_t*)&Vf[((d * 2 + 1) * 64 + lane) * 8];
+      const uint8_t* pv = Vt + vkey * HD + 16 * chunk_slot<HD>(vkey, d) + 8 * vsbit;
+      const v2i32_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) v2i32_t*)(pv));
+      const half8_t c = codes8_to_f16((uint32_t)w[0], (uint32_t)w[1]);
+      const int b = d >> 1;
+      const half8_t sc = {dv[0][b], dv[1][b], dv[2][b], dv[3][b],
+                          dv[4][b], dv[5][b], dv[6][b], dv[7][b]};
+      const half8_t vh = c * sc;
+      const half8_t vl = __builtin_elementwise_fma(c, sc, -vh);
       O[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, phi, O[d], 0, 0, 0);
       O[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl, phi, O[d], 0, 0, 0);
       O[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, plo, O[d], 0, 0, 0);
     }
+    slot = (slot + 1 == D) ? 0 : slot + 1;
   }
+  // copies into the ring past the last tile may still be landing
+  wait_vmcnt<0>();
 
   // ---- epilogue
   const float l_tot = wave_sum_groups(l_part);

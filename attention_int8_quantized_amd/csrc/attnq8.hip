@@ -109,7 +109,8 @@ int check_kv(const void* q, int q_dtype, const int8_t* kc, const uint16_t* ks, c
   if (!head_dim_ok(hd)) return ATTNQ8_EUNSUPPORTED;
   if (hq / hkv > kMaxVectorsPerGroup) return ATTNQ8_EUNSUPPORTED;
   if (kv_stride <= 0) return ATTNQ8_EINVAL;
-  if ((long long)hkv * kv_stride * hd > (1LL << 40)) return ATTNQ8_EINVAL;
+  // per-head cache bytes are addressed with 32-bit buffer offsets
+  if ((long long)kv_stride * hd >= (1LL << 31) - 64) return ATTNQ8_EINVAL;
   if (!aligned(q, 16) || !aligned(kc, 16) || !aligned(vc, 16)) return ATTNQ8_EALIGN;
   if (!aligned(ks, 4) || !aligned(vs, 4)) return ATTNQ8_EALIGN;
   return ATTNQ8_OK;

@@ -11,28 +11,55 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef int v2i32_t __attribute__((ext_vector_type(2)));
 
-// Exact int8 -> fp16 for two codes (the trick described in "hip: gfx12 (RDNA4)
-// WMMA kernel for the int8-KV QSA prompt attention", How): v_perm_b32 places
-// two code bytes in the low byte of each 16-bit half with zero high bytes; xor
-// with 0x64806480 flips each code's sign bit and sets the fp16 exponent field
-// of 1024, so each half reads 1024 + (code + 128); one packed subtraction of
-// 1152 leaves the code.  Every step is exact for all 256 byte values.
-//
-// `sel` is a v_perm_b32 selector whose bytes 1 and 3 are 0x0c (zero) and whose
-// bytes 0 and 2 pick code bytes from the 8-byte value {src_hi : src_lo}.
-__device__ __forceinline__ half2_t codes_to_f16(uint32_t src_hi, uint32_t src_lo, uint32_t sel) {
-  const uint32_t x = __builtin_amdgcn_perm(src_hi, src_lo, sel) ^ 0x64806480u;
-  const half2_t h = __builtin_bit_cast(half2_t, x);
-  const half2_t bias = {(half_t)1152.0f, (half_t)1152.0f};
-  return h - bias;
+// A raw (unswizzled, stride 0) buffer resource over [base, base + bytes):
+// loads at offsets >= bytes return zero and access no memory.  The third
+// descriptor word is the gfx9 data-format setting for raw 32-bit access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }
 
-// Four codes of one dword -> four fp16 values, in byte order.
+// Exact int8 -> fp16 of four codes (the trick described in "hip: gfx12 (RDNA4)
+// WMMA kernel for the int8-KV QSA prompt attention", How, in a gfx9 form): xor
+// 0x80 turns each signed code c into the byte c + 128; v_perm_b32 places two
+// such bytes under an exponent byte 0x64, so each 16-bit half reads
+// 1024 + (c + 128) as fp16; one packed subtraction of 1152 leaves c.  Every
+// step is exact for all 256 byte values.
 __device__ __forceinline__ half4_t dword_codes_to_f16(uint32_t w) {
-  const half2_t a = codes_to_f16(0u, w, 0x0c010c00u);
-  const half2_t b = codes_to_f16(0u, w, 0x0c030c02u);
+  const uint32_t u = w ^ 0x80808080u;
+  const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);  // [c0, c1]
+  const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);  // [c2, c3]
+  const half2_t bias = {(half_t)1152.0f, (half_t)1152.0f};
+  const half2_t a = __builtin_bit_cast(half2_t, lo) - bias;
+  const half2_t b = __builtin_bit_cast(half2_t, hi) - bias;
   return (half4_t){a[0], a[1], b[0], b[1]};
+}
+
+__device__ __forceinline__ half8_t codes8_to_f16(uint32_t w0, uint32_t w1) {
+  const half4_t a = dword_codes_to_f16(w0);
+  const half4_t b = dword_codes_to_f16(w1);
+  return (half8_t){a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Direct-to-LDS loads.  `lds_addr` (wave-uniform) receives 16 (or 4) bytes per
+// lane at lds_addr + 16 * lane (4 * lane) from the lane's buffer offset; an
+// offset past the resource's range stores zeros.  They are issued through
+// inline assembly so that the compiler does not serialise later LDS reads
+// behind them: completion is tracked by the caller with wait_vmcnt<N>().
+__device__ __forceinline__ void dma_b128(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_addr, int voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_addr), "v"(voffset), "s"(rsrc) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_addr, int voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(lds_addr), "v"(voffset), "s"(rsrc) : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
 __device__ __forceinline__ half_t f16_from_bits(uint16_t b) {
