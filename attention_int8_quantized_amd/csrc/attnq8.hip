@@ -14,7 +14,7 @@ namespace {
 
 using namespace attnq8;
 
-constexpr int kMaxVectorsPerGroup = 128;  // 8 waves x 16 query vectors
+constexpr int kMaxVectorsPerGroup = 128;  // query vectors of one row group
 constexpr int kTargetCUs = 256;           // MI355X compute units
 constexpr double kLog2e = 1.4426950408889634;
 
@@ -43,6 +43,26 @@ int launch_status() {
   return e == hipSuccess ? ATTNQ8_OK : ATTNQ8_EHIP;
 }
 
+// Waves per workgroup for a row group of `vectors` query vectors: one wave per
+// 16 vectors, at least four (the conversion of each tile is split over all).
+int waves_for(int vectors) {
+  (void)vectors;
+  return 8;
+}
+
+// Workgroups resident per CU (LDS: ring of kRingDepth tiles + converted tile).
+int wgs_per_cu(int hd) { return hd == 256 ? 1 : (hd == 128 ? 2 : 4); }  // LDS-bound
+
+int splits_for(int n_keys, int units, int hd) {
+  const int tiles = (n_keys + 31) / 32;
+  const int target = kTargetCUs * wgs_per_cu(hd);
+  int s = (target + units - 1) / units;
+  const int cap = tiles / 2;  // at least two 32-key tiles per split
+  if (s > cap) s = cap;
+  if (s < 1) s = 1;
+  return s;
+}
+
 int auto_rows_per_group(int G, int n_rows) {
   int rg = kMaxVectorsPerGroup / G;
   if (rg > n_rows) rg = n_rows;
@@ -50,45 +70,11 @@ int auto_rows_per_group(int G, int n_rows) {
   return rg;
 }
 
-// Rows per workgroup for the prompt path: about four waves of 16 vectors,
-// preferring a whole number of 16-vector tiles.
-int prompt_rows_per_group(int G, int n_queries) {
-  int best = 64 / G;
-  if (best < 1) best = 1;
-  for (int r = best; r >= 1; --r) {
-    if ((r * G) % 16 == 0) {
-      best = r;
-      break;
-    }
-  }
-  if (best > n_queries) best = n_queries;
-  return best;
-}
-
-int splits_for(int n_keys, int n_groups, int n_kv_heads) {
-  const int tiles = (n_keys + 31) / 32;
-  const int units = n_groups * n_kv_heads;
-  int s = (kTargetCUs + units - 1) / units;
-  if (s > tiles) s = tiles;
-  if (s < 1) s = 1;
-  return s;
-}
-
 using KernelFn = void (*)(AttendArgs);
 
 template <int HD, bool QF32, bool FINAL>
 KernelFn pick_nw(int nw) {
-  switch (nw) {
-    case 1: return attend_q8_kernel<HD, 1, QF32, FINAL>;
-    case 2: return attend_q8_kernel<HD, 2, QF32, FINAL>;
-    case 3: return attend_q8_kernel<HD, 3, QF32, FINAL>;
-    case 4: return attend_q8_kernel<HD, 4, QF32, FINAL>;
-    case 5: return attend_q8_kernel<HD, 5, QF32, FINAL>;
-    case 6: return attend_q8_kernel<HD, 6, QF32, FINAL>;
-    case 7: return attend_q8_kernel<HD, 7, QF32, FINAL>;
-    case 8: return attend_q8_kernel<HD, 8, QF32, FINAL>;
-    default: return nullptr;
-  }
+  return nw == 4 ? attend_q8_kernel<HD, 4, QF32, FINAL> : attend_q8_kernel<HD, 8, QF32, FINAL>;
 }
 
 template <bool FINAL>
@@ -141,10 +127,10 @@ int attn_verify_q8_splits(int n_q_heads, int n_kv_heads, int head_dim, int ctx_l
   if (ctx_len < 0 || n_rows < 1 || n_rows > 32) return ATTNQ8_EINVAL;
   const int G = n_q_heads / n_kv_heads;
   if (G > kMaxVectorsPerGroup) return ATTNQ8_EUNSUPPORTED;
+  if (rows_per_group < 0 || rows_per_group * G > kMaxVectorsPerGroup) return ATTNQ8_EINVAL;
   const int rg = rows_per_group > 0 ? rows_per_group : auto_rows_per_group(G, n_rows);
-  if (rows_per_group < 0 || rg * G > kMaxVectorsPerGroup) return ATTNQ8_EINVAL;
   const int groups = (n_rows + rg - 1) / rg;
-  return splits_for(ctx_len + n_rows, groups, n_kv_heads);
+  return splits_for(ctx_len + n_rows, groups * n_kv_heads, head_dim);
 }
 
 size_t attn_verify_q8_workspace_bytes(int n_rows, int n_q_heads, int head_dim, int n_splits) {
@@ -165,12 +151,12 @@ int attn_verify_q8(const void* q, int q_dtype, const int8_t* k_codes, const uint
   if (rows_per_group < 0 || n_splits < 0) return ATTNQ8_EINVAL;
   if (!(sm_scale >= 0.0f) || isinf(sm_scale)) return ATTNQ8_EINVAL;
   const int G = n_q_heads / n_kv_heads;
+  if (rows_per_group * G > kMaxVectorsPerGroup) return ATTNQ8_EINVAL;
   const int rg = rows_per_group > 0 ? rows_per_group : auto_rows_per_group(G, n_rows);
-  if (rg * G > kMaxVectorsPerGroup) return ATTNQ8_EINVAL;
   const int groups = (n_rows + rg - 1) / rg;
   const int n_keys = ctx_len + n_rows;
   const int tiles = (n_keys + 31) / 32;
-  const int S = n_splits > 0 ? n_splits : splits_for(n_keys, groups, n_kv_heads);
+  const int S = n_splits > 0 ? n_splits : splits_for(n_keys, groups * n_kv_heads, head_dim);
   if (S > tiles || S > 65535) return ATTNQ8_EINVAL;
   if (!workspace) return ATTNQ8_EINVAL;
   if (!aligned(workspace, 16)) return ATTNQ8_EALIGN;
@@ -180,7 +166,7 @@ int attn_verify_q8(const void* q, int q_dtype, const int8_t* k_codes, const uint
   st = device_status();
   if (st) return st;
 
-  const int nw = (rg * G + 15) / 16;
+  const int nw = waves_for(rg * G);
   KernelFn fn = pick_kernel<false>(head_dim, q_dtype == ATTNQ8_F32, nw);
   if (!fn) return ATTNQ8_EUNSUPPORTED;
   AttendArgs a;
@@ -250,12 +236,18 @@ int attn_prompt_q8(const void* q, int q_dtype, const int8_t* k_codes, const uint
   if ((long long)q_pos0 + n_queries > kv_len || kv_len > kv_stride) return ATTNQ8_EINVAL;
   if (!(sm_scale >= 0.0f) || isinf(sm_scale)) return ATTNQ8_EINVAL;
   const int G = n_q_heads / n_kv_heads;
-  const int rg = prompt_rows_per_group(G, n_queries);
-  const int groups = (n_queries + rg - 1) / rg;
+  // rows per workgroup: queries whose G heads fill up to 8 waves of 16 vectors,
+  // keeping about one workgroup per CU for the chunk
+  int rq = kMaxVectorsPerGroup / G;
+  if (rq < 1) rq = 1;
+  const int per_cu = (n_queries * n_kv_heads + kTargetCUs - 1) / kTargetCUs;
+  if (rq > per_cu) rq = per_cu;
+  if (rq < 1) rq = 1;
+  const int groups = (n_queries + rq - 1) / rq;
   if (groups > 65535) return ATTNQ8_EINVAL;
   st = device_status();
   if (st) return st;
-  const int nw = (rg * G + 15) / 16;
+  const int nw = waves_for(rq * G);
   KernelFn fn = pick_kernel<true>(head_dim, q_dtype == ATTNQ8_F32, nw);
   if (!fn) return ATTNQ8_EUNSUPPORTED;
   AttendArgs a;
@@ -272,7 +264,7 @@ int attn_prompt_q8(const void* q, int q_dtype, const int8_t* k_codes, const uint
   a.kv_stride = kv_stride;
   a.pos0 = q_pos0;
   a.n_rows = n_queries;
-  a.rows_per_wg = rg;
+  a.rows_per_wg = rq;
   a.n_splits = 1;
   const float scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)head_dim));
   a.kmul = (float)((double)scale * kLog2e);
@@ -281,7 +273,7 @@ int attn_prompt_q8(const void* q, int q_dtype, const int8_t* k_codes, const uint
   if (st) return st;
   snprintf(g_last_path, sizeof(g_last_path),
            "prompt hd%d q%s waves%d rows_per_group%d groups%d kv_heads%d", head_dim,
-           q_dtype == ATTNQ8_F32 ? "f32" : "f16", nw, rg, groups, n_kv_heads);
+           q_dtype == ATTNQ8_F32 ? "f32" : "f16", nw, rq, groups, n_kv_heads);
   return ATTNQ8_OK;
 }
 

@@ -10,12 +10,15 @@ repeats.  Kernel durations come from HIP events recorded on the library's
 stream around each launch; the GPU is held by a spin kernel while the timed
 launches are queued so that host submission latency does not enter them.
 
-Prints one JSON line (rank 0, N=1).
+Prints one JSON line.  Other modes:
+  --copy-calibration   run only plain device copies of a known size (for
+                       scaling the FETCH_SIZE / WRITE_SIZE counters)
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -29,6 +32,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "verify-attn KV GB/s (% HBM peak); prompt-attn TFLOP/s (% MFMA peak)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_BYTES = 1 << 30
 
 
 def parse():
@@ -43,11 +48,47 @@ def parse():
     ap.add_argument("--rows-per-group", type=int, default=0)
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--rotate-bytes", type=float, default=1.1e9)
+    ap.add_argument("--copy-calibration", action="store_true")
     return ap.parse_args()
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: counter results are valid only for this build."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "attention_int8_quantized_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key: str):
+    """Counter-derived HBM bytes per launch, or None when absent or stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("kernels", {}).get(kernel_key)
+
+
+def copy_calibration():
+    import torch
+
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "copy-calibration", "bytes_per_copy": COPY_BYTES, "copies": 3}))
 
 
 def main():
@@ -56,6 +97,9 @@ def main():
         print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
 
@@ -113,7 +157,6 @@ def main():
         if pbufs:
             prompt_call(i)
     torch.cuda.synchronize()
-    verify_path = None
     verify_call(0)
     verify_path = ops.last_path()
     prompt_path = None
@@ -128,8 +171,8 @@ def main():
     ev = [[E() for _ in range(4)] for _ in range(K)]
     t_start, t_end = E(), E()
     torch.cuda.synchronize()
-    # hold the GPU while the launches are queued (~40 us of host time per step)
-    torch.cuda._sleep(int(2.4e9 * (0.05e-3 * K + 0.02) / 1.0))
+    # hold the GPU while the launches are queued (~50 us of host time per step)
+    torch.cuda._sleep(int(2.4e9 * (0.06e-3 * K + 0.02)))
     wall0 = time.perf_counter()
     t_start.record()
     for i in range(K):
@@ -151,12 +194,12 @@ def main():
     kp = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)]) * 1e-3
     step_ms = t_start.elapsed_time(t_end) / K
 
-    vbytes = wv.visible_kv_bytes(args.rows_per_group or None) if wv.kind == "verify" else 0
-    unique = wv.unique_kv_bytes()
+    vbytes = wv.visible_kv_bytes(args.rows_per_group or None)
     verify_s = float(np.mean(k1 + k2))
     gbs = vbytes / verify_s / 1e9
     k1_mean = float(np.mean(k1))
     k1_gbs = vbytes / k1_mean / 1e9
+    tr_v = load_traffic("verify")
 
     res = {
         "metric": METRIC,
@@ -169,7 +212,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8-kv/fp16-mfma/fp32-softmax",
+        "dtype": "int8-kv/fp16-mfma/fp32",
         "data": "synthetic (seeded N(0,1), int8 block-32 quantised KV)",
         "config": {
             "workload": wv.name,
@@ -182,7 +225,7 @@ def main():
             "kernel_us": round(k1_mean * 1e6, 3),
             "reduce_us": round(float(np.mean(k2)) * 1e6, 3),
             "kv_bytes": vbytes,
-            "unique_kv_bytes": unique,
+            "unique_kv_bytes": wv.unique_kv_bytes(),
             "gbs": round(gbs, 2),
             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
         },
@@ -193,7 +236,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": tr_v,
         },
     }
     if pbufs:
@@ -216,7 +259,7 @@ def main():
             "peak": FP16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tf / FP16_MFMA_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": load_traffic("prompt"),
         }
     res["host_wall_s"] = round(wall, 3)
 
@@ -246,7 +289,7 @@ def cpu_baseline(wv, iv):
         oracle.verify(q, iv.k_codes[:1], iv.k_scales[:1], iv.v_codes[:1], iv.v_scales[:1],
                       wv.ctx_len)
         reps += 1
-        if time.perf_counter() - t0 > 10.0 or reps >= 20:
+        if time.perf_counter() - t0 > 10.0 or reps >= 50:
             break
     dt = (time.perf_counter() - t0) / reps
     sample_bytes = wv.visible_kv_bytes() / wv.n_kv_heads
@@ -255,8 +298,8 @@ def cpu_baseline(wv, iv):
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{wv.name}: KV head 0 and its {wv.group} Q heads x {wv.n_rows} rows, "
-                  f"{reps} repetitions, {dt:.3f} s each",
+        "sample": f"{wv.name}: KV head 0 with its {wv.group} Q heads x {wv.n_rows} rows "
+                  f"({sample_bytes} KV bytes), {reps} repetitions of {dt:.3f} s",
     }
 
 
