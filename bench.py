@@ -289,7 +289,7 @@ def cpu_baseline(wv, iv):
         oracle.verify(q, iv.k_codes[:1], iv.k_scales[:1], iv.v_codes[:1], iv.v_scales[:1],
                       wv.ctx_len)
         reps += 1
-        if time.perf_counter() - t0 > 10.0 or reps >= 50:
+        if time.perf_counter() - t0 > 10.0 or reps >= 5000:
             break
     dt = (time.perf_counter() - t0) / reps
     sample_bytes = wv.visible_kv_bytes() / wv.n_kv_heads
