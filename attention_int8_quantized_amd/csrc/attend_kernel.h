@@ -1,29 +1,34 @@
 // The int8-KV attention kernel shared by the verify and prompt paths.
 //
-// One workgroup owns up to NW x 16 query vectors (row, Q head) of a group of
-// consecutive rows that read one KV head -- the "one owner of several query
-// rows shares every K/V scan" organisation of "perf(gfx1100): share Q8 KV scans
-// across verifier rows" (Summary) -- and scans one range of that head's keys
-// in 32-key tiles.  Each of its NW waves owns 16 of the vectors (waves past the
-// last vector only help converting).
+// One workgroup of eight waves owns up to NQ x 16 query vectors (row, Q head)
+// of a group of consecutive rows that read one KV head -- the "one owner of
+// several query rows shares every K/V scan" organisation of "perf(gfx1100):
+// share Q8 KV scans across verifier rows" (Summary) -- and scans one range of
+// that head's keys in 32-key tiles.
 //
-// Per tile:
-//   1. copy: the tile's int8 codes and fp16 scales go from HBM straight into a
-//      ring of DEPTH tiles in LDS (direct-to-LDS buffer loads; the copies of
-//      the next DEPTH-1 tiles are in flight while one is used).  Buffer ranges
-//      end at the split's last key, so the ragged last tile reads zeros.
-//   2. convert, shared by all waves: K codes -> fp16 MFMA fragments (exact);
-//      V codes, read transposed with the gfx950 ds_read_b64_tr_b8, times their
-//      per-key scale -> an exact fp16 hi + lo pair of V^T fragments (dV * code
-//      has at most 18 significant bits; hi is the rounded product, lo the fma
-//      residual).  Each tile is converted once for all the workgroup's vectors.
-//   3. compute, per wave: S^T = K Q^T on v_mfma_f32_16x16x32_f16, one 32-dim
-//      block per MFMA (q in registers, split hi + lo when given in fp32 after
-//      a per-vector power-of-two scaling that keeps both parts normal), each
-//      block's dot scaled by its fp16 K scale in fp32 in fixed block order;
-//      causal / range mask; online softmax in base 2 with a lazily moved
-//      reference point; p split into fp16 hi + lo; O^T += V^T P^T as
-//      (Vhi,Phi) + (Vlo,Phi) + (Vhi,Plo).
+// Per tile t (one workgroup barrier per tile):
+//   copy     the tile's int8 codes and fp16 scales go from HBM straight into a
+//            ring of kRingDepth tiles in LDS (direct-to-LDS buffer loads, the
+//            next tiles in flight); buffer ranges end at the split's last key,
+//            so the ragged last tile reads zeros.
+//   convert  (tile t+1, all waves) K codes -> fp16 MFMA fragments in LDS,
+//            exact; each wave reads its own 32-dim block of V transposed with
+//            the gfx950 ds_read_b64_tr_b8 and keeps dV * code in registers as
+//            an exact fp16 hi + lo pair (dV * code has at most 18 significant
+//            bits; hi is the rounded product, lo the fma residual).
+//   QK       (tile t, one wave per 16 vectors) S^T = K Q^T on
+//            v_mfma_f32_16x16x32_f16, one 32-dim block per MFMA (q in registers,
+//            split hi + lo when given in fp32 after a per-vector power-of-two
+//            scaling that keeps both parts normal), each block's dot scaled by
+//            its fp16 K scale in fp32 in fixed block order; causal / range
+//            mask; online softmax in base 2 with a lazily moved reference point;
+//            p split into fp16 hi + lo and handed to every wave through LDS
+//            with the tile's rescale factor.
+//   PV       (tile t-1, all waves) each wave owns one 32-dim block of the
+//            output for its share of the vectors: O^T *= alpha, then
+//            O^T += V^T P^T as (Vhi,Phi) + (Vlo,Phi) + (Vhi,Plo).
+// PV trails QK by one tile, so the waves that own no vectors and the MFMA
+// work of the output are spread over all four SIMDs of the compute unit.
 //
 // The accuracy contract of "hip: gfx12 (RDNA4) WMMA kernel for the int8-KV QSA
 // prompt attention" (How: fp16 hi+lo of q and p, fixed summation order, online
@@ -65,7 +70,8 @@ struct AttendArgs {
 // above fp16's subnormal range so that their hi + lo split keeps 22 bits.
 constexpr float kRescaleSlack = 15.0f;
 constexpr float kRefBias = 8.0f;
-constexpr int kRingDepth = 3;
+constexpr int kRingDepth = 5;
+constexpr int kWaves = 8;  // waves per workgroup
 
 // LDS layout of one 32-key ring stage (bytes):
 //   K codes  [32 keys][HD]  int8, 16-byte chunks of a row permuted by chunk_slot
@@ -87,21 +93,15 @@ struct Stage {
   static constexpr int R = 16 / C;                            // key rows per 256 bytes
 };
 
-// Converted fragments of one tile (bytes), one 1 KB fragment = 64 lanes x 16 B:
-//   Kf [block b][subtile u]: K codes as fp16, A operand of S^T = K Q^T;
+// MFMA fragments, 64 lanes x 16 B = 1 KB each:
+//   K fragment [block b][subtile u]: K codes as fp16, A operand of S^T = K Q^T;
 //      lane l: key 16u + l%16, dims 32b + 8(l/16) .. +7
-//   Vf [dim tile d][hi|lo]: dV * code as fp16 hi/lo, A operand of O^T += V^T P^T;
-//      lane l: dim 16d + l%16, keys pi(l/16, e), e = 0..7
+//   V^T fragment [dim tile d]: dV * code as fp16 (hi or lo), A operand of
+//      O^T += V^T P^T; lane l: dim 16d + l%16, keys pi(l/16, e), e = 0..7
+//   P^T fragment [vector tile n]: p as fp16 (hi or lo), B operand of the same;
+//      lane l: vector 16n + l%16, keys pi(l/16, e), which are the keys that
+//      the lane holds in the S^T accumulators of its two 16-key subtiles
 //   with pi(h, e) = 4h + e for e < 4 and 16 + 4h + e - 4 for e >= 4.
-template <int HD>
-struct Frags {
-  static constexpr int NB = HD / 32;
-  static constexpr int ND = HD / 16;
-  static constexpr int KF_OFF = 0;
-  static constexpr int VF_OFF = NB * 2 * 1024;
-  static constexpr int BYTES = VF_OFF + ND * 2 * 1024;
-};
-
 // Slot of 16-byte chunk `c` of tile row `key` (0..31) -- an involution in c.
 // Chosen so that the rows read by one 16-lane group -- 16 consecutive keys for
 // K fragments, keys {4h..4h+3, 16+4h..16+4h+3} for the transposing V reads --
@@ -114,8 +114,8 @@ __device__ __forceinline__ int chunk_slot(int key, int c) {
 
 __device__ __forceinline__ int pi_key(int h, int e) { return (e < 4) ? 4 * h + e : 16 + 4 * h + (e - 4); }
 
-// The workgroup's direct-to-LDS copies of one 32-key tile, split over its waves
-// (wave w issues copies w, w + NW, ...).
+// The workgroup's direct-to-LDS copies of one 32-key tile, split over NW of its
+// waves (the one with index w among them issues copies w, w + NW, ...).
 template <int HD, int NW>
 struct TileCopier {
   using L = Stage<HD>;
@@ -181,68 +181,95 @@ template <> struct ScaleRow<2> {
   __device__ __forceinline__ half_t get(int b) const { return v[b]; }
 };
 
-// Convert unit j of a tile (j < NB: V dim tiles 2j, 2j+1; else K block j - NB)
-// from the ring stage `st` into the fragment area `fr`.
+// K codes of block b, subtile u of the ring stage `st` -> the K fragment in `kf`.
 template <int HD>
-__device__ __forceinline__ void convert_unit(int j, const uint8_t* st, uint8_t* fr, int lane) {
+__device__ __forceinline__ void convert_k(int b, int u, const uint8_t* st, uint8_t* kf, int lane) {
   using L = Stage<HD>;
-  using F = Frags<HD>;
+  const int h4 = lane >> 4;
+  const int c = 2 * b + (h4 >> 1);
+  const int key = 16 * u + (lane & 15);
+  const uint2 w = *(const uint2*)(st + L::K_OFF + key * HD + 16 * chunk_slot<HD>(key, c) + 8 * (h4 & 1));
+  *(half8_t*)(kf + ((b * 2 + u) * 64 + lane) * 16) = codes8_to_f16(w.x, w.y);
+}
+
+// V codes of block b (dim tiles 2b, 2b+1) of the ring stage `st`, times their
+// per-key scales -> V^T fragments as exact fp16 hi + lo pairs in registers.
+template <int HD>
+__device__ __forceinline__ void convert_v(int b, const uint8_t* st, int lane, half8_t (&vh)[2], half8_t (&vl)[2]) {
+  using L = Stage<HD>;
   constexpr int NB = L::NB;
   const int h4 = lane >> 4;
-  if (j < NB) {
-    const int b = j;
-    // per-key V scales of block b for keys pi(h4, e)
-    const half_t* vsc = (const half_t*)(st + L::VS_OFF);
-    half8_t sc;
+  // per-key V scales of block b for keys pi(h4, e)
+  const half_t* vsc = (const half_t*)(st + L::VS_OFF);
+  half8_t sc;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sc[e] = vsc[pi_key(h4, e) * NB + b];
-    // transposing reads: lane 16h + 2k + s addresses key pi(h, k), dims 16d + 8s
-    const int vkey = pi_key(h4, (lane & 15) >> 1);
-    const uint8_t* vrow = st + L::V_OFF + vkey * HD + 8 * (lane & 1);
+  for (int e = 0; e < 8; ++e) sc[e] = vsc[pi_key(h4, e) * NB + b];
+  // transposing reads: lane 16h + 2k + s addresses key pi(h, k), dims 16d + 8s
+  const int vkey = pi_key(h4, (lane & 15) >> 1);
+  const uint8_t* vrow = st + L::V_OFF + vkey * HD + 8 * (lane & 1);
 #pragma unroll
-    for (int dd = 0; dd < 2; ++dd) {
-      const int d = 2 * b + dd;
-      const v2i32_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-          (__attribute__((address_space(3))) v2i32_t*)(vrow + 16 * chunk_slot<HD>(vkey, d)));
-      const half8_t c = codes8_to_f16((uint32_t)w[0], (uint32_t)w[1]);
-      const half8_t vh = c * sc;
-      const half8_t vl = __builtin_elementwise_fma(c, sc, -vh);
-      *(half8_t*)(fr + F::VF_OFF + ((d * 2 + 0) * 64 + lane) * 16) = vh;
-      *(half8_t*)(fr + F::VF_OFF + ((d * 2 + 1) * 64 + lane) * 16) = vl;
-    }
-  } else {
-    const int b = j - NB;
-    const int c = 2 * b + (h4 >> 1);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int kk = 16 * u + (lane & 15);
-      const uint2 w = *(const uint2*)(st + L::K_OFF + kk * HD + 16 * chunk_slot<HD>(kk, c) + 8 * (h4 & 1));
-      *(half8_t*)(fr + F::KF_OFF + ((b * 2 + u) * 64 + lane) * 16) = codes8_to_f16(w.x, w.y);
-    }
+  for (int dd = 0; dd < 2; ++dd) {
+    const v2i32_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) v2i32_t*)(vrow + 16 * chunk_slot<HD>(vkey, 2 * b + dd)));
+    const half8_t c = codes8_to_f16((uint32_t)w[0], (uint32_t)w[1]);
+    vh[dd] = c * sc;
+    vl[dd] = __builtin_elementwise_fma(c, sc, -vh[dd]);
   }
 }
 
-// Which wave converts unit j of a tile: waves that own no query vectors take
-// four units for every one a computing wave takes, so that the conversion of
-// the next tile finishes within the computing waves' time on this one.
-__device__ __forceinline__ int convert_owner(int j, int n_compute, int nw) {
-  const int n_idle = nw - n_compute;
-  const int len = 4 * n_idle + n_compute;
-  const int i = j % len;
-  return (i < 4 * n_idle) ? n_compute + (i % n_idle) : i - 4 * n_idle;
-}
+// Work split of a workgroup over its eight waves.  With at most four vector
+// tiles (NQ == 4: verify row groups) the roles are disjoint: waves 0..3 own
+// one vector tile each for QK and convert K; waves 4..7 own NB/4 32-dim blocks
+// each for PV (all vector tiles) and issue the tile copies.  With eight
+// vector tiles (NQ == 8: prompt blocks) every wave owns one block (or, at
+// head_dim 128 and 64, a block for a share of the vector tiles) for PV, the
+// first nq waves also own a vector tile for QK, and every wave converts K.
+// In the disjoint split only the PV waves issue the tile copies, so that the
+// QK waves' loads of q do not queue behind them.
+template <int HD, int NQ>
+struct Roles {
+  static constexpr int NW = kWaves;
+  static constexpr int NB = Stage<HD>::NB;
+  static constexpr bool SPLIT = NQ == 4;
+  static constexpr int BPW = SPLIT ? (NB >= 4 ? NB / 4 : 1) : 1;  // PV blocks per wave
+  static constexpr int GW = SPLIT ? 1 : NW / NB;                  // waves sharing one block
+  static constexpr int NQW = NQ / GW;                             // vector tiles per PV wave
+  static_assert(NQ % GW == 0, "vector tiles must split evenly over the waves");
+  // block j of wave `wave` (>= NB: none)
+  __device__ static int block(int wave, int j) {
+    return SPLIT ? (wave >= 4 ? (wave - 4) + 4 * j : NB) : wave % NB;
+  }
+  // first vector tile of the wave's PV share (then every GW-th)
+  __device__ static int qtile0(int wave) { return SPLIT ? 0 : wave / NB; }
+  // waves that issue the tile copies, and this wave's index among them (< 0: none)
+  static constexpr int NWI = SPLIT ? 4 : NW;
+  __device__ static int copy_index(int wave) { return SPLIT ? wave - 4 : wave; }
+  // waves that convert K, and this wave's index among them (-1: none)
+  __device__ static int k_workers(int nq) { return SPLIT ? 4 : NW; }
+  __device__ static int k_index(int wave, int nq) { return SPLIT ? (wave < 4 ? wave : -1) : wave; }
+};
 
-template <int HD, int NW, bool QF32, bool FINAL>
-__global__ __launch_bounds__(64 * NW) void attend_q8_kernel(const AttendArgs a) {
+// HD: head dim; QF32: q given in fp32 (else fp16); FINAL: write the normalised
+// output (else split partials); NQ: most 16-vector tiles per workgroup.
+template <int HD, bool QF32, bool FINAL, int NQ>
+__global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs a) {
   using L = Stage<HD>;
-  using F = Frags<HD>;
+  using R = Roles<HD, NQ>;
+  constexpr int NW = kWaves;
   constexpr int NB = L::NB;
-  constexpr int ND = HD / 16;  // 16-dim output tiles
   constexpr int D = kRingDepth;
-  constexpr int NU = 2 * NB;   // conversion units per tile
+  constexpr int BPW = R::BPW;
+  constexpr int GW = R::GW;
+  constexpr int NQW = R::NQW;
+  constexpr int KF_BYTES = NB * 2 * 1024;
+  constexpr int PB_BYTES = NQ * 2 * 1024;
+  static_assert(NQ <= NW, "one QK wave per vector tile");
 
   __shared__ __attribute__((aligned(16))) uint8_t ring[D * L::BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t frag[2][F::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t kfrag[2][KF_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t pfrag[2][PB_BYTES];  // [n][hi|lo][lane]
+  __shared__ float alpha_s[2][NQ][16];
+  __shared__ float2 ml_s[NQ][16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -256,40 +283,55 @@ __global__ __launch_bounds__(64 * NW) void attend_q8_kernel(const AttendArgs a) 
   const int r0 = rg * a.rows_per_wg;
   const int nr = min(a.rows_per_wg, a.n_rows - r0);
   const int M = nr * a.G;
+  const int nq = (M + 15) >> 4;         // vector tiles (<= NQ, checked on the host)
   const int n_keys = a.pos0 + r0 + nr;  // keys 0 .. n_keys-1 are seen by some row
   const int n_tiles = (n_keys + 31) >> 5;
   const int t_begin = (int)(((long long)split * n_tiles) / a.n_splits);
   const int t_end = (int)(((long long)(split + 1) * n_tiles) / a.n_splits);
   const int k_end = min(n_keys, t_end * 32);
-  const int n_compute = min(NW, (M + 15) >> 4);  // waves that own query vectors
 
-  // ---- start the copies first so that their latency overlaps the q setup
+  // ---- start the copies first so that their latency overlaps the q setup;
+  // tile t is copied D-2 iterations ahead into ring stage t % D
   const size_t head_rows = (size_t)g * a.kv_stride;
-  TileCopier<HD, NW> cp;
+  constexpr int NWI = R::NWI;
+  const bool copies = R::copy_index(wave) >= 0;  // wave-uniform
+  TileCopier<HD, NWI> cp;
   cp.kc = make_rsrc(a.kc + head_rows * HD, k_end * HD);
   cp.vc = make_rsrc(a.vc + head_rows * HD, k_end * HD);
   cp.ks = make_rsrc(a.ks + head_rows * NB, k_end * NB * 2);
   cp.vs = make_rsrc(a.vs + head_rows * NB, k_end * NB * 2);
-  cp.wave = wave;
+  cp.wave = copies ? R::copy_index(wave) : 0;
   cp.lane = lane;
   const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
+  if (copies) {
 #pragma unroll
-  for (int s = 0; s < D - 1; ++s)
-    cp.issue(ring0 + s * L::BYTES, (t_begin + s) * 32, t_begin + s < t_end);
+    for (int s = 0; s < D - 2; ++s)
+      cp.issue(ring0 + s * L::BYTES, (t_begin + s) * 32, t_begin + s < t_end);
+  }
 
-  // ---- this wave's query vectors: column n16 of its S^T tile
+  // ---- QK role: vector tile `wave` (column n16 of its S^T tile)
+  const bool qk = wave < nq;  // wave-uniform
   const int v = wave * 16 + n16;
-  const bool v_ok = v < M;
-  const bool computes = wave < n_compute;  // wave-uniform
+  const bool v_ok = qk && v < M;
   const int vr = v_ok ? v / a.G : 0;
   const int vh = v_ok ? g * a.G + (v - vr * a.G) : 0;
   const int lim = v_ok ? a.pos0 + r0 + vr : -1;  // last key this vector sees
 
-  // q fragments: B operand of S^T = K Q^T (lane: vector n16, dims 32b + 8*h4 + e)
-  half8_t qhi[NB];
-  half8_t qlo[NB];
-  float xmul;
-  {
+  // Registers held across tiles: the q fragments of the QK role (B operand of
+  // S^T = K Q^T; lane: vector n16, dims 32b + 8*h4 + e; hi in QR(b), lo in
+  // QR(NB + b)) and the O^T accumulators of the PV role (OR(jb, i, dd)).  When
+  // the two roles are on disjoint waves they share the same registers.
+  constexpr int NQREG = QF32 ? 2 * NB : NB;
+  constexpr int NOREG = BPW * NQW * 2;
+  constexpr int OBASE = R::SPLIT ? 0 : NQREG;
+  constexpr int NREG = R::SPLIT ? (NQREG > NOREG ? NQREG : NOREG) : NQREG + NOREG;
+  float4_t regs[NREG];
+#define QR(k) (__builtin_bit_cast(half8_t, regs[(k)]))
+#define OR(jb, i, dd) (regs[OBASE + ((jb) * NQW + (i)) * 2 + (dd)])
+#pragma unroll
+  for (int k = 0; k < NREG; ++k) regs[k] = (float4_t){0, 0, 0, 0};
+  float xmul = 0.0f;
+  if (qk) {
     float qv[NB][8];
     float amax = 0.0f;
     const size_t qoff = ((size_t)(r0 + vr) * a.Hq + vh) * HD + 8 * h4;
@@ -328,201 +370,304 @@ __global__ __launch_bounds__(64 * NW) void attend_q8_kernel(const AttendArgs a) 
     xmul = a.kmul * ldexpf(1.0f, -k);  // exact: a power-of-two factor
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
+      half8_t hi8, lo8;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float x = qv[b][e] * qmul;
         const half_t hi = (half_t)x;
-        qhi[b][e] = hi;
-        qlo[b][e] = QF32 ? (half_t)(x - (float)hi) : (half_t)0.0f;
+        hi8[e] = hi;
+        lo8[e] = (half_t)(x - (float)hi);
       }
+      regs[b] = __builtin_bit_cast(float4_t, hi8);
+      if (QF32) regs[NB + b] = __builtin_bit_cast(float4_t, lo8);
     }
   }
+  float m_ref = -INFINITY;  // QK role: reference point of the vector (base 2)
+  float l_part = 0.0f;      // QK role: this lane's share of the vector's sum
 
-  float4_t O[ND];
-#pragma unroll
-  for (int d = 0; d < ND; ++d) O[d] = (float4_t){0, 0, 0, 0};
-  float m_ref = -INFINITY;
-  float l_part = 0.0f;
+  // ---- PV role: blocks R::block(wave, j), vector tiles q0, q0 + GW, ...
+  const int q0 = R::qtile0(wave);
+  const int kw = R::k_workers(nq);
+  const int ki = R::k_index(wave, nq);
 
-  // ---- prologue: convert the first tile
+  // ---- prologue: K fragments of the first tile
   if (t_begin < t_end) {
-    cp.template wait_all_but<D - 2>();
+    if (copies) cp.template wait_all_but<D - 3>();
     __syncthreads();
-    for (int j = 0; j < NU; ++j)
-      if (convert_owner(j, n_compute, NW) == wave) convert_unit<HD>(j, ring, frag[0], lane);
+    if (ki >= 0)
+      for (int k = ki; k < 2 * NB; k += kw) convert_k<HD>(k >> 1, k & 1, ring, kfrag[t_begin & 1], lane);
   }
 
-  // Per tile t: one barrier, then copy tile t+D-1, convert tile t+1 and
-  // compute tile t (the converted fragments are double-buffered).
-  int slot = 0;
-  int buf = 0;
-  for (int t = t_begin; t < t_end; ++t) {
+  // QK of tile t: S^T, mask, online softmax, P^T fragments and rescale factor
+  // into LDS buffer t & 1.
+  auto qk_tile = [&](int t, const uint8_t* st) {
     const int key0 = t * 32;
-    const bool has_next = t + 1 < t_end;
-    if (has_next) cp.template wait_all_but<D - 3>();  // this wave's copies of tile t+1 landed
-    __syncthreads();  // tile t converted; tile t-1 computed; copies of tile t+1 landed
-    cp.issue(ring0 + ((slot + D - 1) % D) * L::BYTES, key0 + (D - 1) * 32, t + D - 1 < t_end);
-    const uint8_t* st = ring + slot * L::BYTES;
-    if (has_next) {
-      const uint8_t* st_next = ring + ((slot + 1) % D) * L::BYTES;
-      for (int j = 0; j < NU; ++j)
-        if (convert_owner(j, n_compute, NW) == wave) convert_unit<HD>(j, st_next, frag[buf ^ 1], lane);
+    const uint8_t* kf = kfrag[t & 1];
+    // S^T = K Q^T, KG blocks at a time for both 16-key subtiles: K fragments
+    // and key scales first, then the hi MFMAs and the lo MFMAs (each block has
+    // its own accumulator), then the per-block K scales in fp32, in block order
+    constexpr int KG = NB < 4 ? NB : 4;
+    const half_t* Kst = (const half_t*)(st + L::KS_OFF);
+    float4_t s[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+#pragma unroll
+    for (int b0 = 0; b0 < NB; b0 += KG) {
+      half8_t kv[2][KG];
+      ScaleRow<KG> dk[2][4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int j = 0; j < KG; ++j) kv[u][j] = *(const half8_t*)(kf + (((b0 + j) * 2 + u) * 64 + lane) * 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dk[u][e].load(Kst + (16 * u + 4 * h4 + e) * NB + b0);
+      }
+      float4_t acc[2][KG];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < KG; ++j)
+          acc[u][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv[u][j], QR(b0 + j), (float4_t){0, 0, 0, 0}, 0, 0, 0);
+      if (QF32) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int j = 0; j < KG; ++j)
+            acc[u][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv[u][j], QR(NB + b0 + j), acc[u][j], 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < KG; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[u][e] = fmaf((float)dk[u][e].get(j), acc[u][j][e], s[u][e]);
     }
+    // mask and online softmax (base 2), p -> fp16 hi + lo
+    float x[2][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = key0 + 16 * u + 4 * h4 + e;
+        const bool vis = (key < k_end) && (key <= lim);
+        x[u][e] = vis ? s[u][e] * xmul : -INFINITY;
+        tmax = fmaxf(tmax, x[u][e]);
+      }
+    }
+    tmax = wave_max_groups(tmax);
+    const bool need = tmax > m_ref + kRescaleSlack;
+    float alpha = 1.0f;
+    if (__any(need)) {
+      const float m_new = need ? tmax - kRefBias : m_ref;
+      alpha = need ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;
+      l_part *= alpha;
+      m_ref = m_new;
+    }
+    const float mu = (m_ref == -INFINITY) ? 0.0f : m_ref;
+    half8_t phi, plo;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = __builtin_amdgcn_exp2f(x[u][e] - mu);
+        l_part += p;
+        const half_t ph = (half_t)p;
+        phi[4 * u + e] = ph;
+        plo[4 * u + e] = (half_t)(p - (float)ph);
+      }
+    }
+    uint8_t* pf = pfrag[t & 1];
+    *(half8_t*)(pf + ((wave * 2 + 0) * 64 + lane) * 16) = phi;
+    *(half8_t*)(pf + ((wave * 2 + 1) * 64 + lane) * 16) = plo;
+    if (h4 == 0) alpha_s[t & 1][wave][n16] = alpha;
+  };
 
-    if (computes) {
-      const uint8_t* fr = frag[buf];
-      // ---- S^T = K Q^T, per 16-key subtile: the NB hi MFMAs, then the NB lo
-      // MFMAs (independent ones in between), then the per-block K scales
-      const half_t* Kst = (const half_t*)(st + L::KS_OFF);
-      float4_t s[2];
+  // PV of tile t (ring stage st): V^T hi/lo of every owned block from the
+  // ring, then for PG vector tiles at a time O^T *= alpha and
+  // O^T += (Vhi,Phi) + (Vlo,Phi) + (Vhi,Plo).
+  auto pv_tile = [&](int t, const uint8_t* st) {
+    constexpr int PG = NQW < 4 ? NQW : 4;
+    half8_t vh[BPW][2], vl[BPW][2];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        float4_t acc[NB];
+    for (int jb = 0; jb < BPW; ++jb) convert_v<HD>(R::block(wave, jb), st, lane, vh[jb], vl[jb]);
+    const uint8_t* pf = pfrag[t & 1];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const half8_t ka = *(const half8_t*)(fr + F::KF_OFF + ((b * 2 + u) * 64 + lane) * 16);
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qhi[b], (float4_t){0, 0, 0, 0}, 0, 0, 0);
-        }
-        if (QF32) {
+    for (int i0 = 0; i0 < NQW; i0 += PG) {
+      half8_t ph[PG], pl[PG];
+      float al[PG];
+      bool rescale = false;
 #pragma unroll
-          for (int b = 0; b < NB; ++b) {
-            const half8_t ka = *(const half8_t*)(fr + F::KF_OFF + ((b * 2 + u) * 64 + lane) * 16);
-            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qlo[b], acc[b], 0, 0, 0);
+      for (int j = 0; j < PG; ++j) {
+        const int n = min(q0 + GW * (i0 + j), NQ - 1);
+        ph[j] = *(const half8_t*)(pf + ((n * 2 + 0) * 64 + lane) * 16);
+        pl[j] = *(const half8_t*)(pf + ((n * 2 + 1) * 64 + lane) * 16);
+        al[j] = alpha_s[t & 1][n][n16];
+        rescale |= al[j] != 1.0f;
+      }
+      if (__any(rescale)) {
+#pragma unroll
+        for (int jb = 0; jb < BPW; ++jb)
+#pragma unroll
+          for (int j = 0; j < PG; ++j) {
+            OR(jb, i0 + j, 0) *= al[j];
+            OR(jb, i0 + j, 1) *= al[j];
           }
-        }
-        ScaleRow<NB> dk[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dk[e].load(Kst + (16 * u + 4 * h4 + e) * NB);
-        s[u] = (float4_t){0, 0, 0, 0};
-#pragma unroll
-        for (int b = 0; b < NB; ++b)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) s[u][e] = fmaf((float)dk[e].get(b), acc[b][e], s[u][e]);
       }
+#pragma unroll
+      for (int j = 0; j < PG; ++j) {
+        if (q0 + GW * (i0 + j) < nq) {
+#pragma unroll
+          for (int jb = 0; jb < BPW; ++jb)
+#pragma unroll
+            for (int dd = 0; dd < 2; ++dd)
+              OR(jb, i0 + j, dd) = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[jb][dd], ph[j], OR(jb, i0 + j, dd), 0, 0, 0);
+#pragma unroll
+          for (int jb = 0; jb < BPW; ++jb)
+#pragma unroll
+            for (int dd = 0; dd < 2; ++dd)
+              OR(jb, i0 + j, dd) = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl[jb][dd], ph[j], OR(jb, i0 + j, dd), 0, 0, 0);
+#pragma unroll
+          for (int jb = 0; jb < BPW; ++jb)
+#pragma unroll
+            for (int dd = 0; dd < 2; ++dd)
+              OR(jb, i0 + j, dd) = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[jb][dd], pl[j], OR(jb, i0 + j, dd), 0, 0, 0);
+        }
+      }
+    }
+  };
 
-      // ---- mask and online softmax (base 2), p -> fp16 hi + lo
-      float x[2][4];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int key = key0 + 16 * u + 4 * h4 + e;
-          const bool vis = (key < k_end) && (key <= lim);
-          x[u][e] = vis ? s[u][e] * xmul : -INFINITY;
-          tmax = fmaxf(tmax, x[u][e]);
-        }
-      }
-      tmax = wave_max_groups(tmax);
-      const bool need = tmax > m_ref + kRescaleSlack;
-      if (__any(need)) {
-        const float m_new = need ? tmax - kRefBias : m_ref;
-        const float alpha = need ? exp2f(m_ref - m_new) : 1.0f;
-#pragma unroll
-        for (int d = 0; d < ND; ++d) O[d] *= alpha;
-        l_part *= alpha;
-        m_ref = m_new;
-      }
-      const float mu = (m_ref == -INFINITY) ? 0.0f : m_ref;
-      half8_t phi, plo;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p = exp2f(x[u][e] - mu);
-          l_part += p;
-          const half_t ph = (half_t)p;
-          phi[4 * u + e] = ph;
-          plo[4 * u + e] = (half_t)(p - (float)ph);
-        }
-      }
+  // Iteration t: barrier; copy tile t+D-2; QK of tile t; PV of tile t-1;
+  // K fragments of tile t+1.  One extra iteration drains the last PV.
+  int slot = 0;  // ring stage of tile t
+  for (int t = t_begin; t <= t_end; ++t) {
+    const bool has_qk = t < t_end;
+    const bool has_next = t + 1 < t_end;
+    if (has_next && copies) cp.template wait_all_but<D - 4>();  // this wave's copies of tile t+1 landed
+    __syncthreads();  // K(t) converted; P(t-1) written; tile t+1 landed; PV(t-2) done
+    if (has_qk && copies) cp.issue(ring0 + ((slot + D - 2) % D) * L::BYTES, (t + D - 2) * 32, t + D - 2 < t_end);
+    const uint8_t* st = ring + slot * L::BYTES;
+    const uint8_t* st_prev = ring + ((slot + D - 1) % D) * L::BYTES;
+    const bool has_pv = t > t_begin && (!R::SPLIT || R::block(wave, 0) < NB);
 
-      // ---- O^T += V^T P^T: three passes over the dim tiles so that the
-      // MFMAs on one accumulator are separated by independent ones
-#pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        const half8_t vh = *(const half8_t*)(fr + F::VF_OFF + ((d * 2 + 0) * 64 + lane) * 16);
-        O[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, phi, O[d], 0, 0, 0);
-      }
-#pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        const half8_t vl = *(const half8_t*)(fr + F::VF_OFF + ((d * 2 + 1) * 64 + lane) * 16);
-        O[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl, phi, O[d], 0, 0, 0);
-      }
-#pragma unroll
-      for (int d = 0; d < ND; ++d) {
-        const half8_t vh = *(const half8_t*)(fr + F::VF_OFF + ((d * 2 + 0) * 64 + lane) * 16);
-        O[d] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh, plo, O[d], 0, 0, 0);
-      }
+    if (qk && has_qk) qk_tile(t, st);
+    if (has_pv) pv_tile(t - 1, st_prev);
+    if (has_next && ki >= 0) {
+      const uint8_t* stn = ring + ((slot + 1) % D) * L::BYTES;
+      for (int k = ki; k < 2 * NB; k += kw) convert_k<HD>(k >> 1, k & 1, stn, kfrag[(t + 1) & 1], lane);
     }
     slot = (slot + 1 == D) ? 0 : slot + 1;
-    buf ^= 1;
   }
   // copies into the ring past the last tile may still be landing
   wait_vmcnt<0>();
 
-  // ---- epilogue
-  const float l_tot = wave_sum_groups(l_part);
-  if (!v_ok) return;
-  const int row = r0 + vr;
-  if (FINAL) {
-    const float inv_l = 1.0f / l_tot;
-    float* dst = a.out + ((size_t)row * a.Hq + vh) * HD + 4 * h4;
-#pragma unroll
-    for (int d = 0; d < ND; ++d) *(float4_t*)(dst + 16 * d) = O[d] * inv_l;
-  } else {
-    const size_t idx = ((size_t)split * a.n_rows + row) * a.Hq + vh;
-    float* dst = a.part_o + idx * HD + 4 * h4;
-#pragma unroll
-    for (int d = 0; d < ND; ++d) *(float4_t*)(dst + 16 * d) = O[d];
-    if (h4 == 0) a.part_ml[idx] = make_float2(m_ref, l_tot);
+  // ---- epilogue: (m, l) of every vector from its QK wave to the PV waves
+  if (qk) {
+    const float l_tot = wave_sum_groups(l_part);
+    if (h4 == 0) ml_s[wave][n16] = make_float2(m_ref, l_tot);
   }
+  __syncthreads();
+#pragma unroll
+  for (int jb = 0; jb < BPW; ++jb) {
+    const int b = R::block(wave, jb);
+    if (b >= NB) continue;
+#pragma unroll
+    for (int i = 0; i < NQW; ++i) {
+      const int n = q0 + GW * i;
+      const int vv = n * 16 + n16;
+      if (n >= nq || vv >= M) continue;
+      const int orow = r0 + vv / a.G;
+      const int ohead = g * a.G + vv % a.G;
+      const float2 ml = ml_s[n][n16];
+      const int dim0 = 32 * b + 4 * h4;
+      if (FINAL) {
+        const float inv_l = 1.0f / ml.y;
+        float* dst = a.out + ((size_t)orow * a.Hq + ohead) * HD + dim0;
+        *(float4_t*)dst = OR(jb, i, 0) * inv_l;
+        *(float4_t*)(dst + 16) = OR(jb, i, 1) * inv_l;
+      } else {
+        const size_t idx = ((size_t)split * a.n_rows + orow) * a.Hq + ohead;
+        float* dst = a.part_o + idx * HD + dim0;
+        *(float4_t*)dst = OR(jb, i, 0);
+        *(float4_t*)(dst + 16) = OR(jb, i, 1);
+        if (b == 0 && h4 == 0) a.part_ml[idx] = ml;
+      }
+    }
+  }
+#undef QR
+#undef OR
 }
 
-// Merge split partials: one wave per (row, Q head); lane l owns dims 4l..4l+3.
-// Splits are read 16 at a time with all loads in flight, and summed in fixed
-// split order (run-to-run bitwise reproducible).
+// Merge split partials: one 512-thread workgroup per (row, Q head).  The
+// largest reference point over the non-empty splits is found first; then the
+// workgroup's split slots (HD/4 lanes each, 4 dims per lane) accumulate their
+// splits (slot, slot + NSLOT, ...) with up to B loads per lane in flight, and
+// slot 0 adds the slot sums in slot order.  Every order is fixed, so results
+// are run-to-run bitwise reproducible.
+constexpr int kReduceThreads = 512;
 template <int HD>
-__global__ __launch_bounds__(256) void reduce_partials_kernel(const float* __restrict__ part_o,
-                                                              const float2* __restrict__ part_ml,
-                                                              int n_splits, int n_pairs,
-                                                              float* __restrict__ out) {
-  constexpr int NC = HD / 4;  // lanes holding data
-  constexpr int CH = 16;      // splits per batch
-  const int lane = threadIdx.x & 63;
-  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (pair >= n_pairs) return;
+__global__ __launch_bounds__(kReduceThreads) void reduce_partials_kernel(const float* __restrict__ part_o,
+                                                                          const float2* __restrict__ part_ml,
+                                                                          int n_splits, int n_pairs,
+                                                                          float* __restrict__ out) {
+  constexpr int LPS = HD / 4;                    // lanes per split slot
+  constexpr int NSLOT = kReduceThreads / LPS;    // split slots
+  constexpr int NWAVE = kReduceThreads / 64;
+  constexpr int B = 8;                           // splits in flight per lane
+  __shared__ float wmax[NWAVE];
+  __shared__ float4_t slot_acc[NSLOT][LPS];
+  __shared__ float slot_den[NSLOT];
+  const int pair = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+
   float M = -INFINITY;
-  for (int s = lane; s < n_splits; s += 64) {
+  for (int s = tid; s < n_splits; s += kReduceThreads) {
     const float2 ml = part_ml[(size_t)s * n_pairs + pair];
     if (ml.y > 0.0f) M = fmaxf(M, ml.x);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  const bool active = lane < NC;
-  const int dl = active ? lane : 0;
+  if (lane == 0) wmax[tid >> 6] = M;
+  __syncthreads();
+  M = wmax[0];
+#pragma unroll
+  for (int w = 1; w < NWAVE; ++w) M = fmaxf(M, wmax[w]);
+
+  const int slot = tid / LPS;
+  const int dl = tid % LPS;
   float4_t acc = {0, 0, 0, 0};
   float den = 0.0f;
-  for (int s0 = 0; s0 < n_splits; s0 += CH) {
-    float2 ml[CH];
-    float4_t o[CH];
+  for (int s0 = slot; s0 < n_splits; s0 += NSLOT * B) {
+    float2 ml[B];
+    float4_t o[B];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int sp = min(s0 + i, n_splits - 1);
+    for (int i = 0; i < B; ++i) {
+      const int sp = min(s0 + i * NSLOT, n_splits - 1);
       const size_t idx = (size_t)sp * n_pairs + pair;
       ml[i] = part_ml[idx];
       o[i] = *(const float4_t*)(part_o + idx * HD + 4 * dl);
     }
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      if (s0 + i < n_splits) {
+    for (int i = 0; i < B; ++i) {
+      if (s0 + i * NSLOT < n_splits) {
         const float w = (ml[i].y > 0.0f) ? exp2f(ml[i].x - M) : 0.0f;
         den = fmaf(w, ml[i].y, den);
         acc += w * o[i];
       }
     }
   }
-  if (active) *(float4_t*)(out + (size_t)pair * HD + 4 * lane) = acc / den;
+  slot_acc[slot][dl] = acc;
+  if (dl == 0) slot_den[slot] = den;
+  __syncthreads();
+  if (slot == 0) {
+    float4_t a = slot_acc[0][dl];
+    float d = slot_den[0];
+#pragma unroll
+    for (int k = 1; k < NSLOT; ++k) {
+      a += slot_acc[k][dl];
+      d += slot_den[k];
+    }
+    *(float4_t*)(out + (size_t)pair * HD + 4 * dl) = a / d;
+  }
 }
 
 // All 65,536 byte pairs through the code conversion used by the kernels.

@@ -43,15 +43,13 @@ int launch_status() {
   return e == hipSuccess ? ATTNQ8_OK : ATTNQ8_EHIP;
 }
 
-// Waves per workgroup for a row group of `vectors` query vectors: one wave per
-// 16 vectors, at least four (the conversion of each tile is split over all).
-int waves_for(int vectors) {
-  (void)vectors;
-  return 8;
-}
+// Vector-tile capacity of the kernel instance for a row group of `vectors`
+// query vectors (16 per tile): 4 or 8.
+int nq_for(int vectors) { return (vectors + 15) / 16 <= 4 ? 4 : 8; }
 
-// Workgroups resident per CU (LDS: ring of kRingDepth tiles + converted tile).
-int wgs_per_cu(int hd) { return hd == 256 ? 1 : (hd == 128 ? 2 : 4); }  // LDS-bound
+// Workgroups resident per CU: one at head_dim 128 and 256 (registers, LDS),
+// two at head_dim 64.
+int wgs_per_cu(int hd) { return hd == 64 ? 2 : 1; }  // register- and LDS-bound
 
 int splits_for(int n_keys, int units, int hd) {
   const int tiles = (n_keys + 31) / 32;
@@ -63,8 +61,10 @@ int splits_for(int n_keys, int units, int hd) {
   return s;
 }
 
-int auto_rows_per_group(int G, int n_rows) {
-  int rg = kMaxVectorsPerGroup / G;
+// Default row group: every row of a KV head in one workgroup, up to 128 query
+// vectors (64 at head_dim 256, where 128 would not fit the registers).
+int auto_rows_per_group(int G, int n_rows, int hd) {
+  int rg = (hd == 256 ? 64 : kMaxVectorsPerGroup) / G;
   if (rg > n_rows) rg = n_rows;
   if (rg < 1) rg = 1;
   return rg;
@@ -73,16 +73,16 @@ int auto_rows_per_group(int G, int n_rows) {
 using KernelFn = void (*)(AttendArgs);
 
 template <int HD, bool QF32, bool FINAL>
-KernelFn pick_nw(int nw) {
-  return nw == 4 ? attend_q8_kernel<HD, 4, QF32, FINAL> : attend_q8_kernel<HD, 8, QF32, FINAL>;
+KernelFn pick_nq(int nq) {
+  return nq == 4 ? attend_q8_kernel<HD, QF32, FINAL, 4> : attend_q8_kernel<HD, QF32, FINAL, 8>;
 }
 
 template <bool FINAL>
-KernelFn pick_kernel(int hd, bool qf32, int nw) {
+KernelFn pick_kernel(int hd, bool qf32, int nq) {
   switch (hd) {
-    case 64: return qf32 ? pick_nw<64, true, FINAL>(nw) : pick_nw<64, false, FINAL>(nw);
-    case 128: return qf32 ? pick_nw<128, true, FINAL>(nw) : pick_nw<128, false, FINAL>(nw);
-    case 256: return qf32 ? pick_nw<256, true, FINAL>(nw) : pick_nw<256, false, FINAL>(nw);
+    case 64: return qf32 ? pick_nq<64, true, FINAL>(nq) : pick_nq<64, false, FINAL>(nq);
+    case 128: return qf32 ? pick_nq<128, true, FINAL>(nq) : pick_nq<128, false, FINAL>(nq);
+    case 256: return qf32 ? pick_nq<256, true, FINAL>(nq) : pick_nq<256, false, FINAL>(nq);
     default: return nullptr;
   }
 }
@@ -128,7 +128,7 @@ int attn_verify_q8_splits(int n_q_heads, int n_kv_heads, int head_dim, int ctx_l
   const int G = n_q_heads / n_kv_heads;
   if (G > kMaxVectorsPerGroup) return ATTNQ8_EUNSUPPORTED;
   if (rows_per_group < 0 || rows_per_group * G > kMaxVectorsPerGroup) return ATTNQ8_EINVAL;
-  const int rg = rows_per_group > 0 ? rows_per_group : auto_rows_per_group(G, n_rows);
+  const int rg = rows_per_group > 0 ? rows_per_group : auto_rows_per_group(G, n_rows, head_dim);
   const int groups = (n_rows + rg - 1) / rg;
   return splits_for(ctx_len + n_rows, groups * n_kv_heads, head_dim);
 }
@@ -152,7 +152,7 @@ int attn_verify_q8(const void* q, int q_dtype, const int8_t* k_codes, const uint
   if (!(sm_scale >= 0.0f) || isinf(sm_scale)) return ATTNQ8_EINVAL;
   const int G = n_q_heads / n_kv_heads;
   if (rows_per_group * G > kMaxVectorsPerGroup) return ATTNQ8_EINVAL;
-  const int rg = rows_per_group > 0 ? rows_per_group : auto_rows_per_group(G, n_rows);
+  const int rg = rows_per_group > 0 ? rows_per_group : auto_rows_per_group(G, n_rows, head_dim);
   const int groups = (n_rows + rg - 1) / rg;
   const int n_keys = ctx_len + n_rows;
   const int tiles = (n_keys + 31) / 32;
@@ -166,8 +166,8 @@ int attn_verify_q8(const void* q, int q_dtype, const int8_t* k_codes, const uint
   st = device_status();
   if (st) return st;
 
-  const int nw = waves_for(rg * G);
-  KernelFn fn = pick_kernel<false>(head_dim, q_dtype == ATTNQ8_F32, nw);
+  const int nq = nq_for(rg * G);
+  KernelFn fn = pick_kernel<false>(head_dim, q_dtype == ATTNQ8_F32, nq);
   if (!fn) return ATTNQ8_EUNSUPPORTED;
   AttendArgs a;
   a.q = q;
@@ -187,12 +187,12 @@ int attn_verify_q8(const void* q, int q_dtype, const int8_t* k_codes, const uint
   a.n_splits = S;
   const float scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)head_dim));
   a.kmul = (float)((double)scale * kLog2e);
-  hipLaunchKernelGGL(fn, dim3(S, groups, n_kv_heads), dim3(64 * nw), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL(fn, dim3(S, groups, n_kv_heads), dim3(64 * kWaves), 0, (hipStream_t)stream, a);
   st = launch_status();
   if (st) return st;
   snprintf(g_last_path, sizeof(g_last_path),
-           "verify hd%d q%s waves%d rows_per_group%d groups%d splits%d kv_heads%d", head_dim,
-           q_dtype == ATTNQ8_F32 ? "f32" : "f16", nw, rg, groups, S, n_kv_heads);
+           "verify hd%d q%s tiles%d rows_per_group%d groups%d splits%d kv_heads%d", head_dim,
+           q_dtype == ATTNQ8_F32 ? "f32" : "f16", nq, rg, groups, S, n_kv_heads);
   return ATTNQ8_OK;
 }
 
@@ -210,7 +210,7 @@ int attn_reduce_partials(const void* workspace, size_t workspace_bytes, int n_ro
   const float* po = (const float*)workspace;
   const float2* pml =
       (const float2*)((const char*)workspace + (size_t)n_splits * pairs * head_dim * sizeof(float));
-  dim3 grid((pairs + 3) / 4), block(256);
+  dim3 grid(pairs), block(kReduceThreads);
   hipStream_t s = (hipStream_t)stream;
   switch (head_dim) {
     case 64: hipLaunchKernelGGL(reduce_partials_kernel<64>, grid, block, 0, s, po, pml, n_splits, pairs, out); break;
@@ -247,8 +247,8 @@ int attn_prompt_q8(const void* q, int q_dtype, const int8_t* k_codes, const uint
   if (groups > 65535) return ATTNQ8_EINVAL;
   st = device_status();
   if (st) return st;
-  const int nw = waves_for(rq * G);
-  KernelFn fn = pick_kernel<true>(head_dim, q_dtype == ATTNQ8_F32, nw);
+  const int nq = nq_for(rq * G);
+  KernelFn fn = pick_kernel<true>(head_dim, q_dtype == ATTNQ8_F32, nq);
   if (!fn) return ATTNQ8_EUNSUPPORTED;
   AttendArgs a;
   a.q = q;
@@ -268,12 +268,12 @@ int attn_prompt_q8(const void* q, int q_dtype, const int8_t* k_codes, const uint
   a.n_splits = 1;
   const float scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)head_dim));
   a.kmul = (float)((double)scale * kLog2e);
-  hipLaunchKernelGGL(fn, dim3(1, groups, n_kv_heads), dim3(64 * nw), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL(fn, dim3(1, groups, n_kv_heads), dim3(64 * kWaves), 0, (hipStream_t)stream, a);
   st = launch_status();
   if (st) return st;
   snprintf(g_last_path, sizeof(g_last_path),
-           "prompt hd%d q%s waves%d rows_per_group%d groups%d kv_heads%d", head_dim,
-           q_dtype == ATTNQ8_F32 ? "f32" : "f16", nw, rq, groups, n_kv_heads);
+           "prompt hd%d q%s tiles%d rows_per_group%d groups%d kv_heads%d", head_dim,
+           q_dtype == ATTNQ8_F32 ? "f32" : "f16", nq, rq, groups, n_kv_heads);
   return ATTNQ8_OK;
 }
 

@@ -67,10 +67,15 @@ __device__ __forceinline__ half_t f16_from_bits(uint16_t b) {
 }
 
 __device__ __forceinline__ float wave_max_groups(float x) {
-  // max across the four 16-lane groups (lanes l, l^16, l^32, l^48)
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  x = fmaxf(x, __shfl_xor(x, 32, 64));
-  return x;
+  // max across the four 16-lane groups (lanes l, l^16, l^32, l^48) with the
+  // gfx950 lane swaps: a swap of a register with itself returns, per lane,
+  // the lane's own value and its partner's (l^16, then l^32), in some order
+  uint32_t u = __float_as_uint(x);
+  auto r16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  u = __float_as_uint(x);
+  auto r32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 
 __device__ __forceinline__ float wave_sum_groups(float x) {

@@ -39,12 +39,13 @@ def test_workspace_bytes(lib):
 
 def test_auto_splits(lib):
     f = lib.attn_verify_q8_splits
-    # about one workgroup per CU at head_dim 256 (two at 128, four at 64), never
+    # about one workgroup per CU at head_dim 256 and 128 (two at 64), never
     # fewer than two 32-key tiles per split
     assert f(24, 4, 256, 20676, 8, 0) == 64
     assert f(24, 4, 256, 131072, 4, 0) == 64
-    assert f(32, 8, 128, 8192, 32, 0) == 64
-    assert f(32, 8, 128, 8192, 32, 4) == 8
+    assert f(24, 4, 256, 20676, 32, 0) == 16     # at 256, 10 rows (60 vectors) per group: 4 groups
+    assert f(32, 8, 128, 8192, 32, 0) == 32      # one group of 128 vectors per KV head
+    assert f(32, 8, 128, 8192, 32, 4) == 4
     assert f(4, 1, 64, 256, 4, 0) == 4         # 260 keys -> 9 tiles -> at most 4 splits
     assert f(4, 1, 64, 0, 1, 0) == 1
     assert f(4, 3, 64, 10, 4, 0) == _lib.EINVAL
