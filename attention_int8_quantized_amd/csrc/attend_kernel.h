@@ -8,8 +8,8 @@
 //
 // Per tile t (one workgroup barrier per tile):
 //   copy     the tile's int8 codes and fp16 scales go from HBM straight into a
-//            ring of kRingDepth tiles in LDS (direct-to-LDS buffer loads, the
-//            next tiles in flight); buffer ranges end at the split's last key,
+//            ring of tiles in LDS (direct-to-LDS buffer loads, kCopyLead tiles
+//            in flight); buffer ranges end at the split's last key,
 //            so the ragged last tile reads zeros.
 //   convert  (tile t+1, all waves) K codes -> fp16 MFMA fragments in LDS,
 //            exact; each wave reads its own 32-dim block of V transposed with
@@ -70,8 +70,7 @@ struct AttendArgs {
 // above fp16's subnormal range so that their hi + lo split keeps 22 bits.
 constexpr float kRescaleSlack = 15.0f;
 constexpr float kRefBias = 8.0f;
-constexpr int kRingDepth = 5;
-constexpr int kWaves = 8;  // waves per workgroup
+constexpr int kCopyLead = 3;  // tiles in flight ahead of the one being converted
 
 // LDS layout of one 32-key ring stage (bytes):
 //   K codes  [32 keys][HD]  int8, 16-byte chunks of a row permuted by chunk_slot
@@ -115,51 +114,79 @@ __device__ __forceinline__ int chunk_slot(int key, int c) {
 __device__ __forceinline__ int pi_key(int h, int e) { return (e < 4) ? 4 * h + e : 16 + 4 * h + (e - 4); }
 
 // The workgroup's direct-to-LDS copies of one 32-key tile, split over NW of its
-// waves (the one with index w among them issues copies w, w + NW, ...).
+// waves.  A tile is CODE_OPS 1 KB copies of K codes, the same of V codes (the
+// same rows and chunk permutation, so a K copy and a V copy share their lane
+// offsets) and SCALE_OPS copies of each scale plane.  With CODE_OPS >= NW the
+// wave with index w copies code chunks w, w + NW, ... of both planes; with
+// fewer chunks than waves the first CODE_OPS waves copy one chunk of each.  The
+// scale copies go one per wave to the waves after those (or from wave 0 when
+// every wave copies codes).  Offsets are computed once; per tile only the key
+// offset is added.
 template <int HD, int NW>
 struct TileCopier {
   using L = Stage<HD>;
-  static constexpr int MAXC = (L::NOPS + NW - 1) / NW;  // copies per wave (max)
-  static constexpr int MINC = L::NOPS / NW;             // copies per wave (min)
+  static constexpr bool WIDE = L::CODE_OPS >= NW;
+  static constexpr int CPW = WIDE ? L::CODE_OPS / NW : 1;  // code chunks per copying wave
+  static constexpr int NS = 2 * L::SCALE_OPS;              // scale copies per tile
+  static_assert(!WIDE || L::CODE_OPS % NW == 0, "code chunks must split evenly");
+  static_assert((WIDE ? 0 : L::CODE_OPS) + NS <= NW, "one scale copy per wave at most");
 
   __amdgpu_buffer_rsrc_t kc, vc, ks, vs;
-  int wave, lane;
+  int lane;
+  bool codes;        // this wave copies code chunks (wave-uniform)
+  int s_op;          // scale copy of this wave (< 0: none; < SCALE_OPS: K, else V)
+  int code_off[CPW]; // per lane: byte offset of the chunk within the tile's rows
+  uint32_t code_lds[CPW];
+  int s_off;         // per lane: byte offset within the tile's scale plane (< 0: lane idle)
+  uint32_t s_lds;
 
-  __device__ __forceinline__ int count() const { return (L::NOPS - wave + NW - 1) / NW; }
+  __device__ __forceinline__ void init(int w, int lane_) {
+    lane = lane_;
+    codes = WIDE || w < L::CODE_OPS;
+#pragma unroll
+    for (int r = 0; r < CPW; ++r) {
+      const int j = WIDE ? w + NW * r : w;  // chunk index within a plane
+      const int pos = j * 1024 + 16 * lane;
+      const int row = pos / HD;
+      code_off[r] = row * HD + 16 * chunk_slot<HD>(row, (pos % HD) / 16);
+      code_lds[r] = j * 1024;
+    }
+    s_op = w - (WIDE ? 0 : L::CODE_OPS);
+    if (s_op >= NS) s_op = -1;
+    const int jj = s_op % L::SCALE_OPS;
+    const int byte = jj * 256 + 4 * lane;
+    s_off = byte < 2 * HD ? byte : -1;
+    s_lds = (s_op >= L::SCALE_OPS ? L::VS_OFF : L::KS_OFF) + jj * 256;
+  }
+
+  // copies per tile issued by this wave
+  __device__ __forceinline__ int count() const { return (codes ? 2 * CPW : 0) + (s_op >= 0 ? 1 : 0); }
 
   // Copy the tile starting at key0 into the stage at lds (zeros when !live).
   __device__ __forceinline__ void issue(uint32_t lds, int key0, bool live) const {
     constexpr int kOut = 0x7ffffff0;  // past every buffer range: stores zeros
+    if (codes) {
 #pragma unroll
-    for (int i = 0; i < MAXC; ++i) {
-      const int o = wave + i * NW;
-      if (o < L::NOPS) {
-        if (o < 2 * L::CODE_OPS) {
-          const bool is_v = o >= L::CODE_OPS;
-          const int j = is_v ? o - L::CODE_OPS : o;
-          const int pos = j * 1024 + 16 * lane;
-          const int row = pos / HD;
-          const int c = chunk_slot<HD>(row, (pos % HD) / 16);
-          const int off = live ? (key0 + row) * HD + 16 * c : kOut;
-          dma_b128(is_v ? vc : kc, lds + (is_v ? L::V_OFF : L::K_OFF) + j * 1024, off);
-        } else {
-          const int j = o - 2 * L::CODE_OPS;
-          const bool is_v = j >= L::SCALE_OPS;
-          const int jj = is_v ? j - L::SCALE_OPS : j;
-          const int byte = jj * 256 + 4 * lane;
-          const int off = (live && byte < 2 * HD) ? key0 * 2 * L::NB + byte : kOut;
-          if (byte < 2 * HD)
-            dma_b32(is_v ? vs : ks, lds + (is_v ? L::VS_OFF : L::KS_OFF) + jj * 256, off);
-        }
+      for (int r = 0; r < CPW; ++r) {
+        const int off = live ? key0 * HD + code_off[r] : kOut;
+        dma_b128(kc, lds + L::K_OFF + code_lds[r], off);
+        dma_b128(vc, lds + L::V_OFF + code_lds[r], off);
       }
+    }
+    if (s_op >= 0 && s_off >= 0) {
+      const int off = live ? key0 * 2 * L::NB + s_off : kOut;
+      if (s_op < L::SCALE_OPS) dma_b32(ks, lds + s_lds, off);
+      else dma_b32(vs, lds + s_lds, off);
     }
   }
 
   // Wait until this wave's copies of all but the newest `newer` tiles landed.
   template <int newer>
   __device__ __forceinline__ void wait_all_but() const {
-    if (count() == MAXC) wait_vmcnt<MAXC * newer>();
-    else wait_vmcnt<MINC * newer>();
+    if (count() == 2 * CPW + 1) wait_vmcnt<(2 * CPW + 1) * newer>();
+    else if (count() == 2 * CPW) wait_vmcnt<2 * CPW * newer>();
+    else if (count() == 1) wait_vmcnt<newer>();
+    else wait_vmcnt<0>();
   }
 };
 
@@ -218,35 +245,40 @@ __device__ __forceinline__ void convert_v(int b, const uint8_t* st, int lane, ha
 }
 
 // Work split of a workgroup over its eight waves.  With at most four vector
-// tiles (NQ == 4: verify row groups) the roles are disjoint: waves 0..3 own
-// one vector tile each for QK and convert K; waves 4..7 own NB/4 32-dim blocks
-// each for PV (all vector tiles) and issue the tile copies.  With eight
-// vector tiles (NQ == 8: prompt blocks) every wave owns one block (or, at
-// head_dim 128 and 64, a block for a share of the vector tiles) for PV, the
-// first nq waves also own a vector tile for QK, and every wave converts K.
-// In the disjoint split only the PV waves issue the tile copies, so that the
-// QK waves' loads of q do not queue behind them.
+// tiles (NQ <= 4: verify row groups) the roles are disjoint: waves 0..3 own
+// one vector tile each for QK and do nothing else; waves 4..7 own the 32-dim
+// blocks for PV (two each at head_dim 256; at 64 a block for half the vector
+// tiles) and issue the tile copies, so that the QK waves' loads of q do not
+// queue behind those; K is converted by wave 3 when it owns no vector tile
+// (SIMD 3 hosts no QK work), else by the PV waves.  With eight vector tiles
+// (NQ == 8: prompt blocks) every wave owns a block (or a block for a share of
+// the vector tiles) for PV, converts K and issues copies, and the first nq
+// waves also own a vector tile for QK.
+constexpr int kWaves = 8;
+
 template <int HD, int NQ>
 struct Roles {
+  static constexpr bool SPLIT = NQ <= 4;
   static constexpr int NW = kWaves;
+  static constexpr int PV0 = SPLIT ? 4 : 0;  // first PV wave
+  static constexpr int NPV = NW - PV0;       // PV waves
   static constexpr int NB = Stage<HD>::NB;
-  static constexpr bool SPLIT = NQ == 4;
-  static constexpr int BPW = SPLIT ? (NB >= 4 ? NB / 4 : 1) : 1;  // PV blocks per wave
-  static constexpr int GW = SPLIT ? 1 : NW / NB;                  // waves sharing one block
-  static constexpr int NQW = NQ / GW;                             // vector tiles per PV wave
+  static constexpr int BPW = NB > NPV ? NB / NPV : 1;  // PV blocks per wave
+  static constexpr int GW = NPV > NB ? NPV / NB : 1;   // PV waves sharing one block
+  static constexpr int NQW = NQ / GW;                  // vector tiles per PV wave
   static_assert(NQ % GW == 0, "vector tiles must split evenly over the waves");
-  // block j of wave `wave` (>= NB: none)
-  __device__ static int block(int wave, int j) {
-    return SPLIT ? (wave >= 4 ? (wave - 4) + 4 * j : NB) : wave % NB;
-  }
+  // PV block j of wave `wave` (NB: none)
+  __device__ static int block(int wave, int j) { return wave >= PV0 ? (wave - PV0) % NB + NPV * j : NB; }
   // first vector tile of the wave's PV share (then every GW-th)
-  __device__ static int qtile0(int wave) { return SPLIT ? 0 : wave / NB; }
+  __device__ static int qtile0(int wave) { return (wave - PV0) / NB; }
   // waves that issue the tile copies, and this wave's index among them (< 0: none)
-  static constexpr int NWI = SPLIT ? 4 : NW;
-  __device__ static int copy_index(int wave) { return SPLIT ? wave - 4 : wave; }
-  // waves that convert K, and this wave's index among them (-1: none)
-  __device__ static int k_workers(int nq) { return SPLIT ? 4 : NW; }
-  __device__ static int k_index(int wave, int nq) { return SPLIT ? (wave < 4 ? wave : -1) : wave; }
+  static constexpr int NWI = NPV;
+  __device__ static int copy_index(int wave) { return wave - PV0; }
+  // waves that convert K, and this wave's index among them (< 0: none)
+  __device__ static int k_workers(int nq) { return SPLIT && nq < 4 ? 1 : NPV; }
+  __device__ static int k_index(int wave, int nq) {
+    return SPLIT && nq < 4 ? (wave == 3 ? 0 : -1) : wave - PV0;
+  }
 };
 
 // HD: head dim; QF32: q given in fp32 (else fp16); FINAL: write the normalised
@@ -255,9 +287,12 @@ template <int HD, bool QF32, bool FINAL, int NQ>
 __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs a) {
   using L = Stage<HD>;
   using R = Roles<HD, NQ>;
-  constexpr int NW = kWaves;
+  constexpr int NW = R::NW;
   constexpr int NB = L::NB;
-  constexpr int D = kRingDepth;
+  // ring stages: tiles t (QK, V), t+1 (K conversion) and the copies in
+  // flight, plus t-1 where PV converts V^T of its tile when it multiplies it
+  constexpr int LEAD = kCopyLead;
+  constexpr int D = R::SPLIT ? LEAD + 1 : LEAD + 2;
   constexpr int BPW = R::BPW;
   constexpr int GW = R::GW;
   constexpr int NQW = R::NQW;
@@ -270,6 +305,9 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
   __shared__ __attribute__((aligned(16))) uint8_t pfrag[2][PB_BYTES];  // [n][hi|lo][lane]
   __shared__ float alpha_s[2][NQ][16];
   __shared__ float2 ml_s[NQ][16];
+  // split fp32 variant: the q lo fragments of the QK waves [n][b][lane]
+  constexpr bool QLO_LDS = R::SPLIT && QF32;
+  __shared__ __attribute__((aligned(16))) uint8_t qlo_s[QLO_LDS ? NQ * NB * 1024 : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -300,12 +338,11 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
   cp.vc = make_rsrc(a.vc + head_rows * HD, k_end * HD);
   cp.ks = make_rsrc(a.ks + head_rows * NB, k_end * NB * 2);
   cp.vs = make_rsrc(a.vs + head_rows * NB, k_end * NB * 2);
-  cp.wave = copies ? R::copy_index(wave) : 0;
-  cp.lane = lane;
+  cp.init(copies ? R::copy_index(wave) : NWI, lane);
   const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
   if (copies) {
 #pragma unroll
-    for (int s = 0; s < D - 2; ++s)
+    for (int s = 0; s < LEAD; ++s)
       cp.issue(ring0 + s * L::BYTES, (t_begin + s) * 32, t_begin + s < t_end);
   }
 
@@ -316,18 +353,22 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
   const int vr = v_ok ? v / a.G : 0;
   const int vh = v_ok ? g * a.G + (v - vr * a.G) : 0;
   const int lim = v_ok ? a.pos0 + r0 + vr : -1;  // last key this vector sees
+  const int lim_eff = min(lim, k_end - 1);        // ... within this split
 
   // Registers held across tiles: the q fragments of the QK role (B operand of
   // S^T = K Q^T; lane: vector n16, dims 32b + 8*h4 + e; hi in QR(b), lo in
   // QR(NB + b)) and the O^T accumulators of the PV role (OR(jb, i, dd)).  When
-  // the two roles are on disjoint waves they share the same registers.
-  constexpr int NQREG = QF32 ? 2 * NB : NB;
+  // the two roles are on disjoint waves they share the same registers, which
+  // then also hold the PV role's V^T of the next tile (VR(jb, dd, hi|lo)).
+  constexpr int NQREG = QF32 && !QLO_LDS ? 2 * NB : NB;
   constexpr int NOREG = BPW * NQW * 2;
+  constexpr int NVREG = R::SPLIT ? BPW * 2 * 2 : 0;
   constexpr int OBASE = R::SPLIT ? 0 : NQREG;
-  constexpr int NREG = R::SPLIT ? (NQREG > NOREG ? NQREG : NOREG) : NQREG + NOREG;
+  constexpr int NREG = R::SPLIT ? (NQREG > NOREG + NVREG ? NQREG : NOREG + NVREG) : NQREG + NOREG;
   float4_t regs[NREG];
 #define QR(k) (__builtin_bit_cast(half8_t, regs[(k)]))
 #define OR(jb, i, dd) (regs[OBASE + ((jb) * NQW + (i)) * 2 + (dd)])
+#define VR(jb, dd, hl) (regs[NOREG + ((jb) * 2 + (dd)) * 2 + (hl)])
 #pragma unroll
   for (int k = 0; k < NREG; ++k) regs[k] = (float4_t){0, 0, 0, 0};
   float xmul = 0.0f;
@@ -379,7 +420,8 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
         lo8[e] = (half_t)(x - (float)hi);
       }
       regs[b] = __builtin_bit_cast(float4_t, hi8);
-      if (QF32) regs[NB + b] = __builtin_bit_cast(float4_t, lo8);
+      if (QLO_LDS) *(half8_t*)(qlo_s + ((wave * NB + b) * 64 + lane) * 16) = lo8;
+      else if (QF32) regs[NB + b] = __builtin_bit_cast(float4_t, lo8);
     }
   }
   float m_ref = -INFINITY;  // QK role: reference point of the vector (base 2)
@@ -392,7 +434,7 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
 
   // ---- prologue: K fragments of the first tile
   if (t_begin < t_end) {
-    if (copies) cp.template wait_all_but<D - 3>();
+    if (copies) cp.template wait_all_but<LEAD - 1>();
     __syncthreads();
     if (ki >= 0)
       for (int k = ki; k < 2 * NB; k += kw) convert_k<HD>(k >> 1, k & 1, ring, kfrag[t_begin & 1], lane);
@@ -400,13 +442,13 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
 
   // QK of tile t: S^T, mask, online softmax, P^T fragments and rescale factor
   // into LDS buffer t & 1.
-  auto qk_tile = [&](int t, const uint8_t* st) {
+  auto qk_tile = [&](int t, const uint8_t* st, auto&& after_mfma) {
     const int key0 = t * 32;
     const uint8_t* kf = kfrag[t & 1];
     // S^T = K Q^T, KG blocks at a time for both 16-key subtiles: K fragments
     // and key scales first, then the hi MFMAs and the lo MFMAs (each block has
     // its own accumulator), then the per-block K scales in fp32, in block order
-    constexpr int KG = NB < 4 ? NB : 4;
+    constexpr int KG = NB < 4 ? NB : (R::SPLIT ? 2 : 4);  // blocks per group (registers)
     const half_t* Kst = (const half_t*)(st + L::KS_OFF);
     float4_t s[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
@@ -427,11 +469,15 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
         for (int j = 0; j < KG; ++j)
           acc[u][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv[u][j], QR(b0 + j), (float4_t){0, 0, 0, 0}, 0, 0, 0);
       if (QF32) {
+        half8_t ql[KG];
+#pragma unroll
+        for (int j = 0; j < KG; ++j)
+          ql[j] = QLO_LDS ? *(const half8_t*)(qlo_s + ((wave * NB + b0 + j) * 64 + lane) * 16) : QR(NB + b0 + j);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
           for (int j = 0; j < KG; ++j)
-            acc[u][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv[u][j], QR(NB + b0 + j), acc[u][j], 0, 0, 0);
+            acc[u][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv[u][j], ql[j], acc[u][j], 0, 0, 0);
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -440,6 +486,7 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
 #pragma unroll
           for (int e = 0; e < 4; ++e) s[u][e] = fmaf((float)dk[u][e].get(j), acc[u][j][e], s[u][e]);
     }
+    after_mfma();
     // mask and online softmax (base 2), p -> fp16 hi + lo
     float x[2][4];
     float tmax = -INFINITY;
@@ -448,11 +495,13 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int key = key0 + 16 * u + 4 * h4 + e;
-        const bool vis = (key < k_end) && (key <= lim);
-        x[u][e] = vis ? s[u][e] * xmul : -INFINITY;
-        tmax = fmaxf(tmax, x[u][e]);
+        x[u][e] = key <= lim_eff ? s[u][e] * xmul : -INFINITY;
       }
     }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, x[u][e]);
     tmax = wave_max_groups(tmax);
     const bool need = tmax > m_ref + kRescaleSlack;
     float alpha = 1.0f;
@@ -537,22 +586,111 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
 
   // Iteration t: barrier; copy tile t+D-2; QK of tile t; PV of tile t-1;
   // K fragments of tile t+1.  One extra iteration drains the last PV.
+  //
+  // In the disjoint split each wave's work of an iteration is one basic block
+  // so that its loads are issued together and its VALU work overlaps its
+  // MFMAs: a QK wave converts its K units of tile t+1 (unconditionally: past
+  // the last tile the result is never read) between the S^T MFMAs and the
+  // softmax; a PV wave converts V^T of tile t into registers for the next
+  // iteration while it multiplies tile t-1, for all NQ vector tiles (those
+  // past nq hold stale P^T and are never written out).
   int slot = 0;  // ring stage of tile t
   for (int t = t_begin; t <= t_end; ++t) {
     const bool has_qk = t < t_end;
     const bool has_next = t + 1 < t_end;
-    if (has_next && copies) cp.template wait_all_but<D - 4>();  // this wave's copies of tile t+1 landed
+    if (has_next && copies) cp.template wait_all_but<LEAD - 2>();  // this wave's copies of tile t+1 landed
     __syncthreads();  // K(t) converted; P(t-1) written; tile t+1 landed; PV(t-2) done
-    if (has_qk && copies) cp.issue(ring0 + ((slot + D - 2) % D) * L::BYTES, (t + D - 2) * 32, t + D - 2 < t_end);
+    if (has_qk && copies) cp.issue(ring0 + ((slot + LEAD) % D) * L::BYTES, (t + LEAD) * 32, t + LEAD < t_end);
     const uint8_t* st = ring + slot * L::BYTES;
     const uint8_t* st_prev = ring + ((slot + D - 1) % D) * L::BYTES;
-    const bool has_pv = t > t_begin && (!R::SPLIT || R::block(wave, 0) < NB);
+    const uint8_t* stn = ring + ((slot + 1) % D) * L::BYTES;
+    uint8_t* kfn = kfrag[(t + 1) & 1];
 
-    if (qk && has_qk) qk_tile(t, st);
-    if (has_pv) pv_tile(t - 1, st_prev);
-    if (has_next && ki >= 0) {
-      const uint8_t* stn = ring + ((slot + 1) % D) * L::BYTES;
-      for (int k = ki; k < 2 * NB; k += kw) convert_k<HD>(k >> 1, k & 1, stn, kfrag[(t + 1) & 1], lane);
+    if constexpr (R::SPLIT) {
+      if (wave < R::PV0) {
+        if (qk && has_qk) qk_tile(t, st, [] {});
+        else if (ki == 0 && has_next) {
+          constexpr int KB = 2 * NB < 4 ? 2 * NB : 4;  // units per batch (registers)
+#pragma unroll 1
+          for (int k0 = 0; k0 < 2 * NB; k0 += KB)
+#pragma unroll
+            for (int j = 0; j < KB; ++j) convert_k<HD>((k0 + j) >> 1, (k0 + j) & 1, stn, kfn, lane);
+        }
+      } else {
+        // K units of tile t+1 (unconditionally: past the last tile the result
+        // is never read), V^T of tile t into registers, PV of tile t-1
+        auto kconv = [&]() {
+          if (kw == R::NPV) {
+#pragma unroll
+            for (int j = 0; j < (2 * NB + R::NPV - 1) / R::NPV; ++j) {
+              const int k = ki + R::NPV * j;
+              if ((2 * NB) % R::NPV == 0 || k < 2 * NB) convert_k<HD>(k >> 1, k & 1, stn, kfn, lane);
+            }
+          }
+        };
+        if (t == t_begin) {
+#pragma unroll
+          for (int jb = 0; jb < BPW; ++jb) {
+            half8_t vnh[2], vnl[2];
+            convert_v<HD>(R::block(wave, jb), st, lane, vnh, vnl);
+#pragma unroll
+            for (int dd = 0; dd < 2; ++dd) {
+              VR(jb, dd, 0) = __builtin_bit_cast(float4_t, vnh[dd]);
+              VR(jb, dd, 1) = __builtin_bit_cast(float4_t, vnl[dd]);
+            }
+          }
+          kconv();
+        } else {
+          const uint8_t* pf = pfrag[(t - 1) & 1];
+          half8_t ph[NQW], pl[NQW];
+          float al[NQW];
+          bool rescale = false;
+#pragma unroll
+          for (int i = 0; i < NQW; ++i) {
+            const int n = q0 + GW * i;
+            ph[i] = *(const half8_t*)(pf + ((n * 2 + 0) * 64 + lane) * 16);
+            pl[i] = *(const half8_t*)(pf + ((n * 2 + 1) * 64 + lane) * 16);
+            al[i] = alpha_s[(t - 1) & 1][n][n16];
+            rescale |= al[i] != 1.0f;
+          }
+          half8_t vnh[BPW][2], vnl[BPW][2];
+#pragma unroll
+          for (int jb = 0; jb < BPW; ++jb) convert_v<HD>(R::block(wave, jb), st, lane, vnh[jb], vnl[jb]);
+          kconv();
+          if (__any(rescale)) {
+#pragma unroll
+            for (int jb = 0; jb < BPW; ++jb)
+#pragma unroll
+              for (int i = 0; i < NQW; ++i) {
+                OR(jb, i, 0) *= al[i];
+                OR(jb, i, 1) *= al[i];
+              }
+          }
+#pragma unroll
+          for (int hl = 0; hl < 3; ++hl)
+#pragma unroll
+            for (int i = 0; i < NQW; ++i)
+#pragma unroll
+              for (int jb = 0; jb < BPW; ++jb)
+#pragma unroll
+                for (int dd = 0; dd < 2; ++dd)
+                  OR(jb, i, dd) = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                      __builtin_bit_cast(half8_t, VR(jb, dd, hl == 1)), hl == 2 ? pl[i] : ph[i], OR(jb, i, dd), 0, 0, 0);
+#pragma unroll
+          for (int jb = 0; jb < BPW; ++jb)
+#pragma unroll
+            for (int dd = 0; dd < 2; ++dd) {
+              VR(jb, dd, 0) = __builtin_bit_cast(float4_t, vnh[jb][dd]);
+              VR(jb, dd, 1) = __builtin_bit_cast(float4_t, vnl[jb][dd]);
+            }
+        }
+      }
+    } else {
+      const bool has_pv = t > t_begin;
+      if (qk && has_qk) qk_tile(t, st, [] {});
+      if (has_pv) pv_tile(t - 1, st_prev);
+      if (has_next)
+        for (int k = ki; k < 2 * NB; k += kw) convert_k<HD>(k >> 1, k & 1, stn, kfn, lane);
     }
     slot = (slot + 1 == D) ? 0 : slot + 1;
   }
@@ -594,6 +732,7 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
   }
 #undef QR
 #undef OR
+#undef VR
 }
 
 // Merge split partials: one 512-thread workgroup per (row, Q head).  The

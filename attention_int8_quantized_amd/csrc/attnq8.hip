@@ -44,8 +44,15 @@ int launch_status() {
 }
 
 // Vector-tile capacity of the kernel instance for a row group of `vectors`
-// query vectors (16 per tile): 4 or 8.
-int nq_for(int vectors) { return (vectors + 15) / 16 <= 4 ? 4 : 8; }
+// query vectors (16 per tile): the smallest instance that holds them (at
+// head_dim 128 and 64 the instances below 8 hold 2 or 4 and 4 tiles).
+int nq_for(int vectors, int hd) {
+  const int n = (vectors + 15) / 16;
+  if (n > 4) return 8;
+  if (hd == 256) return n <= 2 ? 2 : n;
+  if (hd == 128) return n <= 2 ? 2 : 4;
+  return 4;
+}
 
 // Workgroups resident per CU: one at head_dim 128 and 256 (registers, LDS),
 // two at head_dim 64.
@@ -74,7 +81,13 @@ using KernelFn = void (*)(AttendArgs);
 
 template <int HD, bool QF32, bool FINAL>
 KernelFn pick_nq(int nq) {
-  return nq == 4 ? attend_q8_kernel<HD, QF32, FINAL, 4> : attend_q8_kernel<HD, QF32, FINAL, 8>;
+  switch (nq) {
+    case 2: if constexpr (HD >= 128) return attend_q8_kernel<HD, QF32, FINAL, 2>; else return nullptr;
+    case 3: if constexpr (HD == 256) return attend_q8_kernel<HD, QF32, FINAL, 3>; else return nullptr;
+    case 4: return attend_q8_kernel<HD, QF32, FINAL, 4>;
+    case 8: return attend_q8_kernel<HD, QF32, FINAL, 8>;
+    default: return nullptr;
+  }
 }
 
 template <bool FINAL>
@@ -166,7 +179,7 @@ int attn_verify_q8(const void* q, int q_dtype, const int8_t* k_codes, const uint
   st = device_status();
   if (st) return st;
 
-  const int nq = nq_for(rg * G);
+  const int nq = nq_for(rg * G, head_dim);
   KernelFn fn = pick_kernel<false>(head_dim, q_dtype == ATTNQ8_F32, nq);
   if (!fn) return ATTNQ8_EUNSUPPORTED;
   AttendArgs a;
@@ -247,7 +260,7 @@ int attn_prompt_q8(const void* q, int q_dtype, const int8_t* k_codes, const uint
   if (groups > 65535) return ATTNQ8_EINVAL;
   st = device_status();
   if (st) return st;
-  const int nq = nq_for(rq * G);
+  const int nq = nq_for(rq * G, head_dim);
   KernelFn fn = pick_kernel<true>(head_dim, q_dtype == ATTNQ8_F32, nq);
   if (!fn) return ATTNQ8_EUNSUPPORTED;
   AttendArgs a;
