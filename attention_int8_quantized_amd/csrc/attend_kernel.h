@@ -642,40 +642,45 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
           kconv();
         } else {
           const uint8_t* pf = pfrag[(t - 1) & 1];
-          half8_t ph[NQW], pl[NQW];
-          float al[NQW];
-          bool rescale = false;
-#pragma unroll
-          for (int i = 0; i < NQW; ++i) {
-            const int n = q0 + GW * i;
-            ph[i] = *(const half8_t*)(pf + ((n * 2 + 0) * 64 + lane) * 16);
-            pl[i] = *(const half8_t*)(pf + ((n * 2 + 1) * 64 + lane) * 16);
-            al[i] = alpha_s[(t - 1) & 1][n][n16];
-            rescale |= al[i] != 1.0f;
-          }
           half8_t vnh[BPW][2], vnl[BPW][2];
 #pragma unroll
           for (int jb = 0; jb < BPW; ++jb) convert_v<HD>(R::block(wave, jb), st, lane, vnh[jb], vnl[jb]);
           kconv();
-          if (__any(rescale)) {
+          // vector tiles in groups of PG (registers)
+          constexpr int PG = NQW * BPW > 6 ? 2 : NQW;
 #pragma unroll
-            for (int jb = 0; jb < BPW; ++jb)
+          for (int i0 = 0; i0 < NQW; i0 += PG) {
+            half8_t ph[PG], pl[PG];
+            float al[PG];
+            bool rescale = false;
 #pragma unroll
-              for (int i = 0; i < NQW; ++i) {
-                OR(jb, i, 0) *= al[i];
-                OR(jb, i, 1) *= al[i];
-              }
-          }
-#pragma unroll
-          for (int hl = 0; hl < 3; ++hl)
-#pragma unroll
-            for (int i = 0; i < NQW; ++i)
+            for (int j = 0; j < PG; ++j) {
+              const int n = min(q0 + GW * (i0 + j), NQ - 1);
+              ph[j] = *(const half8_t*)(pf + ((n * 2 + 0) * 64 + lane) * 16);
+              pl[j] = *(const half8_t*)(pf + ((n * 2 + 1) * 64 + lane) * 16);
+              al[j] = alpha_s[(t - 1) & 1][n][n16];
+              rescale |= al[j] != 1.0f;
+            }
+            if (__any(rescale)) {
 #pragma unroll
               for (int jb = 0; jb < BPW; ++jb)
 #pragma unroll
-                for (int dd = 0; dd < 2; ++dd)
-                  OR(jb, i, dd) = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                      __builtin_bit_cast(half8_t, VR(jb, dd, hl == 1)), hl == 2 ? pl[i] : ph[i], OR(jb, i, dd), 0, 0, 0);
+                for (int j = 0; j < PG; ++j) {
+                  OR(jb, i0 + j, 0) *= al[j];
+                  OR(jb, i0 + j, 1) *= al[j];
+                }
+            }
+#pragma unroll
+            for (int hl = 0; hl < 3; ++hl)
+#pragma unroll
+              for (int j = 0; j < PG; ++j)
+#pragma unroll
+                for (int jb = 0; jb < BPW; ++jb)
+#pragma unroll
+                  for (int dd = 0; dd < 2; ++dd)
+                    OR(jb, i0 + j, dd) = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        __builtin_bit_cast(half8_t, VR(jb, dd, hl == 1)), hl == 2 ? pl[j] : ph[j], OR(jb, i0 + j, dd), 0, 0, 0);
+          }
 #pragma unroll
           for (int jb = 0; jb < BPW; ++jb)
 #pragma unroll
