@@ -162,19 +162,20 @@ struct TileCopier {
   // copies per tile issued by this wave
   __device__ __forceinline__ int count() const { return (codes ? 2 * CPW : 0) + (s_op >= 0 ? 1 : 0); }
 
-  // Copy the tile starting at key0 into the stage at lds (zeros when !live).
+  // Copy the tile starting at key0 into the stage at lds (zeros when !live:
+  // the key offset then lies past every buffer range).
   __device__ __forceinline__ void issue(uint32_t lds, int key0, bool live) const {
-    constexpr int kOut = 0x7ffffff0;  // past every buffer range: stores zeros
+    const int k0 = live ? key0 : (1 << 22);  // wave-uniform
     if (codes) {
 #pragma unroll
       for (int r = 0; r < CPW; ++r) {
-        const int off = live ? key0 * HD + code_off[r] : kOut;
+        const int off = k0 * HD + code_off[r];
         dma_b128(kc, lds + L::K_OFF + code_lds[r], off);
         dma_b128(vc, lds + L::V_OFF + code_lds[r], off);
       }
     }
     if (s_op >= 0 && s_off >= 0) {
-      const int off = live ? key0 * 2 * L::NB + s_off : kOut;
+      const int off = k0 * 2 * L::NB + s_off;
       if (s_op < L::SCALE_OPS) dma_b32(ks, lds + s_lds, off);
       else dma_b32(vs, lds + s_lds, off);
     }
@@ -436,8 +437,7 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
   if (t_begin < t_end) {
     if (copies) cp.template wait_all_but<LEAD - 1>();
     __syncthreads();
-    if (ki >= 0)
-      for (int k = ki; k < 2 * NB; k += kw) convert_k<HD>(k >> 1, k & 1, ring, kfrag[t_begin & 1], lane);
+    for (int k = wave; k < 2 * NB; k += NW) convert_k<HD>(k >> 1, k & 1, ring, kfrag[t_begin & 1], lane);
   }
 
   // QK of tile t: S^T, mask, online softmax, P^T fragments and rescale factor
@@ -740,26 +740,28 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
 #undef VR
 }
 
-// Merge split partials: one 512-thread workgroup per (row, Q head).  The
-// largest reference point over the non-empty splits is found first; then the
-// workgroup's split slots (HD/4 lanes each, 4 dims per lane) accumulate their
-// splits (slot, slot + NSLOT, ...) with up to B loads per lane in flight, and
-// slot 0 adds the slot sums in slot order.  Every order is fixed, so results
-// are run-to-run bitwise reproducible.
-constexpr int kReduceThreads = 512;
+// Merge split partials: one 256-thread workgroup per (row, Q head, 64-dim
+// chunk).  The largest reference point over the non-empty splits is found
+// first; then the workgroup's 16 split slots (16 lanes each, 4 dims per lane)
+// accumulate their splits (slot, slot + 16, ...) with up to B loads per lane in
+// flight, and slot 0 adds the slot sums in slot order.  Every order is fixed,
+// so results are run-to-run bitwise reproducible.
+constexpr int kReduceThreads = 256;
+constexpr int kReduceDims = 64;  // dims per workgroup
 template <int HD>
 __global__ __launch_bounds__(kReduceThreads) void reduce_partials_kernel(const float* __restrict__ part_o,
                                                                           const float2* __restrict__ part_ml,
                                                                           int n_splits, int n_pairs,
                                                                           float* __restrict__ out) {
-  constexpr int LPS = HD / 4;                    // lanes per split slot
-  constexpr int NSLOT = kReduceThreads / LPS;    // split slots
+  constexpr int LPS = kReduceDims / 4;          // lanes per split slot
+  constexpr int NSLOT = kReduceThreads / LPS;   // split slots
   constexpr int NWAVE = kReduceThreads / 64;
-  constexpr int B = 8;                           // splits in flight per lane
+  constexpr int B = 8;                          // splits in flight per lane
   __shared__ float wmax[NWAVE];
   __shared__ float4_t slot_acc[NSLOT][LPS];
   __shared__ float slot_den[NSLOT];
   const int pair = blockIdx.x;
+  const int dim0 = blockIdx.y * kReduceDims;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
 
@@ -788,7 +790,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_partials_kernel(const f
       const int sp = min(s0 + i * NSLOT, n_splits - 1);
       const size_t idx = (size_t)sp * n_pairs + pair;
       ml[i] = part_ml[idx];
-      o[i] = *(const float4_t*)(part_o + idx * HD + 4 * dl);
+      o[i] = *(const float4_t*)(part_o + idx * HD + dim0 + 4 * dl);
     }
 #pragma unroll
     for (int i = 0; i < B; ++i) {
@@ -810,7 +812,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_partials_kernel(const f
       a += slot_acc[k][dl];
       d += slot_den[k];
     }
-    *(float4_t*)(out + (size_t)pair * HD + 4 * dl) = a / d;
+    *(float4_t*)(out + (size_t)pair * HD + dim0 + 4 * dl) = a / d;
   }
 }
 

@@ -223,7 +223,7 @@ int attn_reduce_partials(const void* workspace, size_t workspace_bytes, int n_ro
   const float* po = (const float*)workspace;
   const float2* pml =
       (const float2*)((const char*)workspace + (size_t)n_splits * pairs * head_dim * sizeof(float));
-  dim3 grid(pairs), block(kReduceThreads);
+  dim3 grid(pairs, head_dim / kReduceDims), block(kReduceThreads);
   hipStream_t s = (hipStream_t)stream;
   switch (head_dim) {
     case 64: hipLaunchKernelGGL(reduce_partials_kernel<64>, grid, block, 0, s, po, pml, n_splits, pairs, out); break;
