@@ -307,7 +307,7 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
   __shared__ float alpha_s[2][NQ][16];
   __shared__ float2 ml_s[NQ][16];
   // split fp32 variant: the q lo fragments of the QK waves [n][b][lane]
-  constexpr bool QLO_LDS = R::SPLIT && QF32;
+  constexpr bool QLO_LDS = false;
   __shared__ __attribute__((aligned(16))) uint8_t qlo_s[QLO_LDS ? NQ * NB * 1024 : 16];
 
   const int tid = threadIdx.x;
@@ -358,18 +358,15 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
 
   // Registers held across tiles: the q fragments of the QK role (B operand of
   // S^T = K Q^T; lane: vector n16, dims 32b + 8*h4 + e; hi in QR(b), lo in
-  // QR(NB + b)) and the O^T accumulators of the PV role (OR(jb, i, dd)).  When
-  // the two roles are on disjoint waves they share the same registers, which
-  // then also hold the PV role's V^T of the next tile (VR(jb, dd, hi|lo)).
+  // QR(NB + b)) and, when the roles share waves, the O^T accumulators of the
+  // PV role (OR(jb, i, dd)); with disjoint roles each role's loop keeps its
+  // own registers.
   constexpr int NQREG = QF32 && !QLO_LDS ? 2 * NB : NB;
-  constexpr int NOREG = BPW * NQW * 2;
-  constexpr int NVREG = R::SPLIT ? BPW * 2 * 2 : 0;
-  constexpr int OBASE = R::SPLIT ? 0 : NQREG;
-  constexpr int NREG = R::SPLIT ? (NQREG > NOREG + NVREG ? NQREG : NOREG + NVREG) : NQREG + NOREG;
+  constexpr int NOREG = R::SPLIT ? 0 : BPW * NQW * 2;
+  constexpr int NREG = NQREG + NOREG;
   float4_t regs[NREG];
 #define QR(k) (__builtin_bit_cast(half8_t, regs[(k)]))
-#define OR(jb, i, dd) (regs[OBASE + ((jb) * NQW + (i)) * 2 + (dd)])
-#define VR(jb, dd, hl) (regs[NOREG + ((jb) * 2 + (dd)) * 2 + (hl)])
+#define OR(jb, i, dd) (regs[NQREG + ((jb) * NQW + (i)) * 2 + (dd)])
 #pragma unroll
   for (int k = 0; k < NREG; ++k) regs[k] = (float4_t){0, 0, 0, 0};
   float xmul = 0.0f;
@@ -585,40 +582,53 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
   };
 
   // Iteration t: barrier; copy tile t+D-2; QK of tile t; PV of tile t-1;
-  // K fragments of tile t+1.  One extra iteration drains the last PV.
-  //
-  // In the disjoint split each wave's work of an iteration is one basic block
-  // so that its loads are issued together and its VALU work overlaps its
-  // MFMAs: a QK wave converts its K units of tile t+1 (unconditionally: past
-  // the last tile the result is never read) between the S^T MFMAs and the
-  // softmax; a PV wave converts V^T of tile t into registers for the next
-  // iteration while it multiplies tile t-1, for all NQ vector tiles (those
-  // past nq hold stale P^T and are never written out).
-  int slot = 0;  // ring stage of tile t
-  for (int t = t_begin; t <= t_end; ++t) {
-    const bool has_qk = t < t_end;
-    const bool has_next = t + 1 < t_end;
-    if (has_next && copies) cp.template wait_all_but<LEAD - 2>();  // this wave's copies of tile t+1 landed
-    __syncthreads();  // K(t) converted; P(t-1) written; tile t+1 landed; PV(t-2) done
-    if (has_qk && copies) cp.issue(ring0 + ((slot + LEAD) % D) * L::BYTES, (t + LEAD) * 32, t + LEAD < t_end);
-    const uint8_t* st = ring + slot * L::BYTES;
-    const uint8_t* st_prev = ring + ((slot + D - 1) % D) * L::BYTES;
-    const uint8_t* stn = ring + ((slot + 1) % D) * L::BYTES;
-    uint8_t* kfn = kfrag[(t + 1) & 1];
-
-    if constexpr (R::SPLIT) {
-      if (wave < R::PV0) {
-        if (qk && has_qk) qk_tile(t, st, [] {});
-        else if (ki == 0 && has_next) {
+  // K fragments of tile t+1.  One extra iteration drains the last PV.  Every
+  // wave passes the same barriers: one per iteration and one before the
+  // output.
+  if constexpr (R::SPLIT) {
+    if (wave < R::PV0) {
+      // ---- QK waves (and wave 3 converting K when it owns no vector tile)
+      int slot = 0;  // ring stage of tile t
+      for (int t = t_begin; t <= t_end; ++t) {
+        __syncthreads();  // K(t) converted; P(t-2) consumed
+        const uint8_t* st = ring + slot * L::BYTES;
+        const uint8_t* stn = ring + ((slot + 1) % D) * L::BYTES;
+        if (qk && t < t_end) {
+          qk_tile(t, st, [] {});
+        } else if (ki == 0 && t + 1 < t_end) {
+          uint8_t* kfn = kfrag[(t + 1) & 1];
           constexpr int KB = 2 * NB < 4 ? 2 * NB : 4;  // units per batch (registers)
 #pragma unroll 1
           for (int k0 = 0; k0 < 2 * NB; k0 += KB)
 #pragma unroll
             for (int j = 0; j < KB; ++j) convert_k<HD>((k0 + j) >> 1, (k0 + j) & 1, stn, kfn, lane);
         }
-      } else {
-        // K units of tile t+1 (unconditionally: past the last tile the result
-        // is never read), V^T of tile t into registers, PV of tile t-1
+        slot = (slot + 1 == D) ? 0 : slot + 1;
+      }
+      if (qk) {
+        const float l_tot = wave_sum_groups(l_part);
+        if (h4 == 0) ml_s[wave][n16] = make_float2(m_ref, l_tot);
+      }
+      __syncthreads();
+    } else {
+      // ---- PV waves: copies, K units of tile t+1 (unconditionally: past the
+      // last tile the result is never read; only when wave 3 does not convert
+      // K), V^T of tile t into registers for the next iteration, PV of tile t-1
+      float4_t O[BPW][NQW][2];
+#pragma unroll
+      for (int jb = 0; jb < BPW; ++jb)
+#pragma unroll
+        for (int i = 0; i < NQW; ++i) O[jb][i][0] = O[jb][i][1] = (float4_t){0, 0, 0, 0};
+      half8_t vch[BPW][2], vcl[BPW][2];
+      int slot = 0;  // ring stage of tile t
+      for (int t = t_begin; t <= t_end; ++t) {
+        const bool has_qk = t < t_end;
+        if (t + 1 < t_end) cp.template wait_all_but<LEAD - 2>();  // this wave's copies of tile t+1 landed
+        __syncthreads();  // K(t) converted; P(t-1) written; tile t+1 landed
+        if (has_qk) cp.issue(ring0 + ((slot + LEAD) % D) * L::BYTES, (t + LEAD) * 32, t + LEAD < t_end);
+        const uint8_t* st = ring + slot * L::BYTES;
+        const uint8_t* stn = ring + ((slot + 1) % D) * L::BYTES;
+        uint8_t* kfn = kfrag[(t + 1) & 1];
         auto kconv = [&]() {
           if (kw == R::NPV) {
 #pragma unroll
@@ -628,24 +638,12 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
             }
           }
         };
-        if (t == t_begin) {
+        half8_t vnh[BPW][2], vnl[BPW][2];
 #pragma unroll
-          for (int jb = 0; jb < BPW; ++jb) {
-            half8_t vnh[2], vnl[2];
-            convert_v<HD>(R::block(wave, jb), st, lane, vnh, vnl);
-#pragma unroll
-            for (int dd = 0; dd < 2; ++dd) {
-              VR(jb, dd, 0) = __builtin_bit_cast(float4_t, vnh[dd]);
-              VR(jb, dd, 1) = __builtin_bit_cast(float4_t, vnl[dd]);
-            }
-          }
-          kconv();
-        } else {
+        for (int jb = 0; jb < BPW; ++jb) convert_v<HD>(R::block(wave, jb), st, lane, vnh[jb], vnl[jb]);
+        kconv();
+        if (t > t_begin) {
           const uint8_t* pf = pfrag[(t - 1) & 1];
-          half8_t vnh[BPW][2], vnl[BPW][2];
-#pragma unroll
-          for (int jb = 0; jb < BPW; ++jb) convert_v<HD>(R::block(wave, jb), st, lane, vnh[jb], vnl[jb]);
-          kconv();
           // vector tiles in groups of PG (registers)
           constexpr int PG = NQW * BPW > 6 ? 2 : NQW;
 #pragma unroll
@@ -666,8 +664,8 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
               for (int jb = 0; jb < BPW; ++jb)
 #pragma unroll
                 for (int j = 0; j < PG; ++j) {
-                  OR(jb, i0 + j, 0) *= al[j];
-                  OR(jb, i0 + j, 1) *= al[j];
+                  O[jb][i0 + j][0] *= al[j];
+                  O[jb][i0 + j][1] *= al[j];
                 }
             }
 #pragma unroll
@@ -678,66 +676,105 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
                 for (int jb = 0; jb < BPW; ++jb)
 #pragma unroll
                   for (int dd = 0; dd < 2; ++dd)
-                    OR(jb, i0 + j, dd) = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        __builtin_bit_cast(half8_t, VR(jb, dd, hl == 1)), hl == 2 ? pl[j] : ph[j], OR(jb, i0 + j, dd), 0, 0, 0);
+                    O[jb][i0 + j][dd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        hl == 1 ? vcl[jb][dd] : vch[jb][dd], hl == 2 ? pl[j] : ph[j], O[jb][i0 + j][dd], 0, 0, 0);
           }
+        }
 #pragma unroll
-          for (int jb = 0; jb < BPW; ++jb)
+        for (int jb = 0; jb < BPW; ++jb)
 #pragma unroll
-            for (int dd = 0; dd < 2; ++dd) {
-              VR(jb, dd, 0) = __builtin_bit_cast(float4_t, vnh[jb][dd]);
-              VR(jb, dd, 1) = __builtin_bit_cast(float4_t, vnl[jb][dd]);
-            }
+          for (int dd = 0; dd < 2; ++dd) {
+            vch[jb][dd] = vnh[jb][dd];
+            vcl[jb][dd] = vnl[jb][dd];
+          }
+        slot = (slot + 1 == D) ? 0 : slot + 1;
+      }
+      // copies into the ring past the last tile may still be landing
+      wait_vmcnt<0>();
+      __syncthreads();  // (m, l) of every vector written by its QK wave
+#pragma unroll
+      for (int jb = 0; jb < BPW; ++jb) {
+        const int b = R::block(wave, jb);
+#pragma unroll
+        for (int i = 0; i < NQW; ++i) {
+          const int n = q0 + GW * i;
+          const int vv = n * 16 + n16;
+          if (n >= nq || vv >= M) continue;
+          const int orow = r0 + vv / a.G;
+          const int ohead = g * a.G + vv % a.G;
+          const float2 ml = ml_s[n][n16];
+          const int dim0 = 32 * b + 4 * h4;
+          if (FINAL) {
+            const float inv_l = 1.0f / ml.y;
+            float* dst = a.out + ((size_t)orow * a.Hq + ohead) * HD + dim0;
+            *(float4_t*)dst = O[jb][i][0] * inv_l;
+            *(float4_t*)(dst + 16) = O[jb][i][1] * inv_l;
+          } else {
+            const size_t idx = ((size_t)split * a.n_rows + orow) * a.Hq + ohead;
+            float* dst = a.part_o + idx * HD + dim0;
+            *(float4_t*)dst = O[jb][i][0];
+            *(float4_t*)(dst + 16) = O[jb][i][1];
+            if (b == 0 && h4 == 0) a.part_ml[idx] = ml;
+          }
         }
       }
-    } else {
-      const bool has_pv = t > t_begin;
-      if (qk && has_qk) qk_tile(t, st, [] {});
-      if (has_pv) pv_tile(t - 1, st_prev);
-      if (has_next)
-        for (int k = ki; k < 2 * NB; k += kw) convert_k<HD>(k >> 1, k & 1, stn, kfn, lane);
     }
-    slot = (slot + 1 == D) ? 0 : slot + 1;
-  }
-  // copies into the ring past the last tile may still be landing
-  wait_vmcnt<0>();
+  } else {
+    int slot = 0;  // ring stage of tile t
+    for (int t = t_begin; t <= t_end; ++t) {
+      const bool has_qk = t < t_end;
+      const bool has_next = t + 1 < t_end;
+      if (has_next) cp.template wait_all_but<LEAD - 2>();  // this wave's copies of tile t+1 landed
+      __syncthreads();  // K(t) converted; P(t-1) written; tile t+1 landed; PV(t-2) done
+      if (has_qk) cp.issue(ring0 + ((slot + LEAD) % D) * L::BYTES, (t + LEAD) * 32, t + LEAD < t_end);
+      const uint8_t* st = ring + slot * L::BYTES;
+      const uint8_t* st_prev = ring + ((slot + D - 1) % D) * L::BYTES;
+      const uint8_t* stn = ring + ((slot + 1) % D) * L::BYTES;
+      if (qk && has_qk) qk_tile(t, st, [] {});
+      if (t > t_begin) pv_tile(t - 1, st_prev);
+      if (has_next)
+        for (int k = ki; k < 2 * NB; k += kw) convert_k<HD>(k >> 1, k & 1, stn, kfrag[(t + 1) & 1], lane);
+      slot = (slot + 1 == D) ? 0 : slot + 1;
+    }
+    // copies into the ring past the last tile may still be landing
+    wait_vmcnt<0>();
 
-  // ---- epilogue: (m, l) of every vector from its QK wave to the PV waves
-  if (qk) {
-    const float l_tot = wave_sum_groups(l_part);
-    if (h4 == 0) ml_s[wave][n16] = make_float2(m_ref, l_tot);
-  }
-  __syncthreads();
+    // ---- epilogue: (m, l) of every vector from its QK wave to the PV waves
+    if (qk) {
+      const float l_tot = wave_sum_groups(l_part);
+      if (h4 == 0) ml_s[wave][n16] = make_float2(m_ref, l_tot);
+    }
+    __syncthreads();
 #pragma unroll
-  for (int jb = 0; jb < BPW; ++jb) {
-    const int b = R::block(wave, jb);
-    if (b >= NB) continue;
+    for (int jb = 0; jb < BPW; ++jb) {
+      const int b = R::block(wave, jb);
+      if (b >= NB) continue;
 #pragma unroll
-    for (int i = 0; i < NQW; ++i) {
-      const int n = q0 + GW * i;
-      const int vv = n * 16 + n16;
-      if (n >= nq || vv >= M) continue;
-      const int orow = r0 + vv / a.G;
-      const int ohead = g * a.G + vv % a.G;
-      const float2 ml = ml_s[n][n16];
-      const int dim0 = 32 * b + 4 * h4;
-      if (FINAL) {
-        const float inv_l = 1.0f / ml.y;
-        float* dst = a.out + ((size_t)orow * a.Hq + ohead) * HD + dim0;
-        *(float4_t*)dst = OR(jb, i, 0) * inv_l;
-        *(float4_t*)(dst + 16) = OR(jb, i, 1) * inv_l;
-      } else {
-        const size_t idx = ((size_t)split * a.n_rows + orow) * a.Hq + ohead;
-        float* dst = a.part_o + idx * HD + dim0;
-        *(float4_t*)dst = OR(jb, i, 0);
-        *(float4_t*)(dst + 16) = OR(jb, i, 1);
-        if (b == 0 && h4 == 0) a.part_ml[idx] = ml;
+      for (int i = 0; i < NQW; ++i) {
+        const int n = q0 + GW * i;
+        const int vv = n * 16 + n16;
+        if (n >= nq || vv >= M) continue;
+        const int orow = r0 + vv / a.G;
+        const int ohead = g * a.G + vv % a.G;
+        const float2 ml = ml_s[n][n16];
+        const int dim0 = 32 * b + 4 * h4;
+        if (FINAL) {
+          const float inv_l = 1.0f / ml.y;
+          float* dst = a.out + ((size_t)orow * a.Hq + ohead) * HD + dim0;
+          *(float4_t*)dst = OR(jb, i, 0) * inv_l;
+          *(float4_t*)(dst + 16) = OR(jb, i, 1) * inv_l;
+        } else {
+          const size_t idx = ((size_t)split * a.n_rows + orow) * a.Hq + ohead;
+          float* dst = a.part_o + idx * HD + dim0;
+          *(float4_t*)dst = OR(jb, i, 0);
+          *(float4_t*)(dst + 16) = OR(jb, i, 1);
+          if (b == 0 && h4 == 0) a.part_ml[idx] = ml;
+        }
       }
     }
   }
 #undef QR
 #undef OR
-#undef VR
 }
 
 // Merge split partials: one 256-thread workgroup per (row, Q head, 64-dim
