@@ -355,6 +355,12 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
   const int vh = v_ok ? g * a.G + (v - vr * a.G) : 0;
   const int lim = v_ok ? a.pos0 + r0 + vr : -1;  // last key this vector sees
   const int lim_eff = min(lim, k_end - 1);        // ... within this split
+  // the smallest of those over the wave's vectors (wave-uniform): tiles that end
+  // at or before it need no mask
+  int lim_min = v_ok ? lim_eff : 0x7fffffff;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) lim_min = min(lim_min, __shfl_xor(lim_min, o, 64));
+  lim_min = __builtin_amdgcn_readfirstlane(lim_min);
 
   // Registers held across tiles: the q fragments of the QK role (B operand of
   // S^T = K Q^T; lane: vector n16, dims 32b + 8*h4 + e; hi in QR(b), lo in
@@ -485,14 +491,23 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
     }
     after_mfma();
     // mask and online softmax (base 2), p -> fp16 hi + lo
+    // (lanes past the last vector of the wave hold q = 0, hence finite values
+    // that only reach their own, never written, outputs)
     float x[2][4];
     float tmax = -INFINITY;
+    if (key0 + 31 <= lim_min) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = key0 + 16 * u + 4 * h4 + e;
-        x[u][e] = key <= lim_eff ? s[u][e] * xmul : -INFINITY;
+        for (int e = 0; e < 4; ++e) x[u][e] = s[u][e] * xmul;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int key = key0 + 16 * u + 4 * h4 + e;
+          x[u][e] = key <= lim_eff ? s[u][e] * xmul : -INFINITY;
+        }
       }
     }
 #pragma unroll
@@ -509,17 +524,25 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
       m_ref = m_new;
     }
     const float mu = (m_ref == -INFINITY) ? 0.0f : m_ref;
-    half8_t phi, plo;
+    // p split into fp16 hi + lo, two at a time: hi truncated (any hi works:
+    // p - hi is exact in fp32 and its fp16 rounding keeps 22 bits of p)
+    float p[8];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float p = __builtin_amdgcn_exp2f(x[u][e] - mu);
-        l_part += p;
-        const half_t ph = (half_t)p;
-        phi[4 * u + e] = ph;
-        plo[4 * u + e] = (half_t)(p - (float)ph);
+        p[4 * u + e] = __builtin_amdgcn_exp2f(x[u][e] - mu);
+        l_part += p[4 * u + e];
       }
+    half8_t phi, plo;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const half2_t h = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(p[i], p[i + 1]));
+      const half2_t l = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(p[i] - (float)h[0], p[i + 1] - (float)h[1]));
+      phi[i] = h[0];
+      phi[i + 1] = h[1];
+      plo[i] = l[0];
+      plo[i + 1] = l[1];
     }
     uint8_t* pf = pfrag[t & 1];
     *(half8_t*)(pf + ((wave * 2 + 0) * 64 + lane) * 16) = phi;
