@@ -40,6 +40,8 @@
 // key its rows see, the normalised output.
 #pragma once
 
+#include <type_traits>
+
 #include "device_utils.h"
 
 namespace attnq8 {
@@ -264,20 +266,33 @@ struct Roles {
   static constexpr int PV0 = SPLIT ? 4 : 0;  // first PV wave
   static constexpr int NPV = NW - PV0;       // PV waves
   static constexpr int NB = Stage<HD>::NB;
-  static constexpr int BPW = NB > NPV ? NB / NPV : 1;  // PV blocks per wave
+  // Six vector tiles at head_dim 256 (a prompt block of 8 queries x 12 heads):
+  // the QK waves 0..5 sit two per SIMD on SIMDs 0 and 1 and one per SIMD on 2
+  // and 3, so the blocks go 0, 0, 1, 1, 1, 1, 2, 2 to waves 0..7 and waves 0
+  // and 1 convert K instead.
+  static constexpr bool UNEVEN = !SPLIT && NQ == 6 && NB == 8;
+  static constexpr int BPW = UNEVEN ? 2 : (NB > NPV ? NB / NPV : 1);  // PV blocks per wave (most)
   static constexpr int GW = NPV > NB ? NPV / NB : 1;   // PV waves sharing one block
   static constexpr int NQW = NQ / GW;                  // vector tiles per PV wave
   static_assert(NQ % GW == 0, "vector tiles must split evenly over the waves");
   // PV block j of wave `wave` (NB: none)
-  __device__ static int block(int wave, int j) { return wave >= PV0 ? (wave - PV0) % NB + NPV * j : NB; }
+  __device__ static int block(int wave, int j) {
+    if (UNEVEN) {
+      if (wave < 2) return NB;
+      if (wave < 6) return j == 0 ? wave - 2 : NB;
+      return 4 + 2 * (wave - 6) + j;
+    }
+    return wave >= PV0 ? (wave - PV0) % NB + NPV * j : NB;
+  }
   // first vector tile of the wave's PV share (then every GW-th)
   __device__ static int qtile0(int wave) { return (wave - PV0) / NB; }
   // waves that issue the tile copies, and this wave's index among them (< 0: none)
   static constexpr int NWI = NPV;
   __device__ static int copy_index(int wave) { return wave - PV0; }
   // waves that convert K, and this wave's index among them (< 0: none)
-  __device__ static int k_workers(int nq) { return SPLIT && nq < 4 ? 1 : NPV; }
+  __device__ static int k_workers(int nq) { return SPLIT && nq < 4 ? 1 : (UNEVEN ? 2 : NPV); }
   __device__ static int k_index(int wave, int nq) {
+    if (UNEVEN) return wave < 2 ? wave : -1;
     return SPLIT && nq < 4 ? (wave == 3 ? 0 : -1) : wave - PV0;
   }
 };
@@ -362,17 +377,12 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
   for (int o = 32; o > 0; o >>= 1) lim_min = min(lim_min, __shfl_xor(lim_min, o, 64));
   lim_min = __builtin_amdgcn_readfirstlane(lim_min);
 
-  // Registers held across tiles: the q fragments of the QK role (B operand of
+  // The q fragments of the QK role, held across tiles (B operand of
   // S^T = K Q^T; lane: vector n16, dims 32b + 8*h4 + e; hi in QR(b), lo in
-  // QR(NB + b)) and, when the roles share waves, the O^T accumulators of the
-  // PV role (OR(jb, i, dd)); with disjoint roles each role's loop keeps its
-  // own registers.
-  constexpr int NQREG = QF32 && !QLO_LDS ? 2 * NB : NB;
-  constexpr int NOREG = R::SPLIT ? 0 : BPW * NQW * 2;
-  constexpr int NREG = NQREG + NOREG;
+  // QR(NB + b)).  Each role loop below keeps its own accumulators.
+  constexpr int NREG = QF32 && !QLO_LDS ? 2 * NB : NB;
   float4_t regs[NREG];
 #define QR(k) (__builtin_bit_cast(half8_t, regs[(k)]))
-#define OR(jb, i, dd) (regs[NQREG + ((jb) * NQW + (i)) * 2 + (dd)])
 #pragma unroll
   for (int k = 0; k < NREG; ++k) regs[k] = (float4_t){0, 0, 0, 0};
   float xmul = 0.0f;
@@ -433,6 +443,9 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
 
   // ---- PV role: blocks R::block(wave, j), vector tiles q0, q0 + GW, ...
   const int q0 = R::qtile0(wave);
+  int nblk = 0;  // PV blocks of this wave (wave-uniform)
+#pragma unroll
+  for (int jb = 0; jb < BPW; ++jb) nblk += R::block(wave, jb) < NB;
   const int kw = R::k_workers(nq);
   const int ki = R::k_index(wave, nq);
 
@@ -451,7 +464,7 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
     // S^T = K Q^T, KG blocks at a time for both 16-key subtiles: K fragments
     // and key scales first, then the hi MFMAs and the lo MFMAs (each block has
     // its own accumulator), then the per-block K scales in fp32, in block order
-    constexpr int KG = NB < 4 ? NB : (R::SPLIT ? 2 : 4);  // blocks per group (registers)
+    constexpr int KG = NB < 4 ? NB : (R::SPLIT || R::UNEVEN ? 2 : 4);  // blocks per group (registers)
     const half_t* Kst = (const half_t*)(st + L::KS_OFF);
     float4_t s[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
@@ -553,11 +566,13 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
   // PV of tile t (ring stage st): V^T hi/lo of every owned block from the
   // ring, then for PG vector tiles at a time O^T *= alpha and
   // O^T += (Vhi,Phi) + (Vlo,Phi) + (Vhi,Plo).
-  auto pv_tile = [&](int t, const uint8_t* st) {
-    constexpr int PG = NQW < 4 ? NQW : 4;
-    half8_t vh[BPW][2], vl[BPW][2];
+  // (Oa: float4_t[NBL][NQW][2], the accumulators of the NBL blocks this wave owns)
+  auto pv_tile = [&](int t, const uint8_t* st, auto& Oa) {
+    constexpr int NBL = std::extent<std::remove_reference_t<decltype(Oa)>>::value;
+    constexpr int PG = NBL > 1 ? 2 : (NQW < 4 ? NQW : 4);  // vector tiles per group (registers)
+    half8_t vh[NBL][2], vl[NBL][2];
 #pragma unroll
-    for (int jb = 0; jb < BPW; ++jb) convert_v<HD>(R::block(wave, jb), st, lane, vh[jb], vl[jb]);
+    for (int jb = 0; jb < NBL; ++jb) convert_v<HD>(R::block(wave, jb), st, lane, vh[jb], vl[jb]);
     const uint8_t* pf = pfrag[t & 1];
 #pragma unroll
     for (int i0 = 0; i0 < NQW; i0 += PG) {
@@ -574,31 +589,31 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
       }
       if (__any(rescale)) {
 #pragma unroll
-        for (int jb = 0; jb < BPW; ++jb)
+        for (int jb = 0; jb < NBL; ++jb)
 #pragma unroll
           for (int j = 0; j < PG; ++j) {
-            OR(jb, i0 + j, 0) *= al[j];
-            OR(jb, i0 + j, 1) *= al[j];
+            Oa[jb][i0 + j][0] *= al[j];
+            Oa[jb][i0 + j][1] *= al[j];
           }
       }
 #pragma unroll
       for (int j = 0; j < PG; ++j) {
         if (q0 + GW * (i0 + j) < nq) {
 #pragma unroll
-          for (int jb = 0; jb < BPW; ++jb)
+          for (int jb = 0; jb < NBL; ++jb)
 #pragma unroll
             for (int dd = 0; dd < 2; ++dd)
-              OR(jb, i0 + j, dd) = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[jb][dd], ph[j], OR(jb, i0 + j, dd), 0, 0, 0);
+              Oa[jb][i0 + j][dd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[jb][dd], ph[j], Oa[jb][i0 + j][dd], 0, 0, 0);
 #pragma unroll
-          for (int jb = 0; jb < BPW; ++jb)
-#pragma unroll
-            for (int dd = 0; dd < 2; ++dd)
-              OR(jb, i0 + j, dd) = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl[jb][dd], ph[j], OR(jb, i0 + j, dd), 0, 0, 0);
-#pragma unroll
-          for (int jb = 0; jb < BPW; ++jb)
+          for (int jb = 0; jb < NBL; ++jb)
 #pragma unroll
             for (int dd = 0; dd < 2; ++dd)
-              OR(jb, i0 + j, dd) = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[jb][dd], pl[j], OR(jb, i0 + j, dd), 0, 0, 0);
+              Oa[jb][i0 + j][dd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl[jb][dd], ph[j], Oa[jb][i0 + j][dd], 0, 0, 0);
+#pragma unroll
+          for (int jb = 0; jb < NBL; ++jb)
+#pragma unroll
+            for (int dd = 0; dd < 2; ++dd)
+              Oa[jb][i0 + j][dd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[jb][dd], pl[j], Oa[jb][i0 + j][dd], 0, 0, 0);
         }
       }
     }
@@ -743,61 +758,86 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
       }
     }
   } else {
-    int slot = 0;  // ring stage of tile t
-    for (int t = t_begin; t <= t_end; ++t) {
-      const bool has_qk = t < t_end;
-      const bool has_next = t + 1 < t_end;
-      if (has_next) cp.template wait_all_but<LEAD - 2>();  // this wave's copies of tile t+1 landed
-      __syncthreads();  // K(t) converted; P(t-1) written; tile t+1 landed; PV(t-2) done
-      if (has_qk) cp.issue(ring0 + ((slot + LEAD) % D) * L::BYTES, (t + LEAD) * 32, t + LEAD < t_end);
-      const uint8_t* st = ring + slot * L::BYTES;
-      const uint8_t* st_prev = ring + ((slot + D - 1) % D) * L::BYTES;
-      const uint8_t* stn = ring + ((slot + 1) % D) * L::BYTES;
-      if (qk && has_qk) qk_tile(t, st, [] {});
-      if (t > t_begin) pv_tile(t - 1, st_prev);
-      if (has_next)
-        for (int k = ki; k < 2 * NB; k += kw) convert_k<HD>(k >> 1, k & 1, stn, kfrag[(t + 1) & 1], lane);
-      slot = (slot + 1 == D) ? 0 : slot + 1;
-    }
-    // copies into the ring past the last tile may still be landing
-    wait_vmcnt<0>();
+    // Each role runs its own loop (same barriers: one per iteration, one before
+    // the output), so that its registers never meet another role's.
+    auto role_loop = [&](auto do_qk, auto do_k, auto& Oa) {
+      constexpr int NBL = std::extent<std::remove_reference_t<decltype(Oa)>>::value;
+#pragma unroll
+      for (int jb = 0; jb < NBL; ++jb)
+#pragma unroll
+        for (int i = 0; i < NQW; ++i) Oa[jb][i][0] = Oa[jb][i][1] = (float4_t){0, 0, 0, 0};
+      int slot = 0;  // ring stage of tile t
+      for (int t = t_begin; t <= t_end; ++t) {
+        const bool has_qk = t < t_end;
+        const bool has_next = t + 1 < t_end;
+        if (has_next) cp.template wait_all_but<LEAD - 2>();  // this wave's copies of tile t+1 landed
+        __syncthreads();  // K(t) converted; P(t-1) written; tile t+1 landed; PV(t-2) done
+        if (has_qk) cp.issue(ring0 + ((slot + LEAD) % D) * L::BYTES, (t + LEAD) * 32, t + LEAD < t_end);
+        const uint8_t* st = ring + slot * L::BYTES;
+        const uint8_t* st_prev = ring + ((slot + D - 1) % D) * L::BYTES;
+        const uint8_t* stn = ring + ((slot + 1) % D) * L::BYTES;
+        if (decltype(do_qk)::value && qk && has_qk) qk_tile(t, st, [] {});
+        if (nblk > 0 && t > t_begin) pv_tile(t - 1, st_prev, Oa);
+        if (decltype(do_k)::value && has_next)
+          for (int k = ki; k < 2 * NB; k += kw) convert_k<HD>(k >> 1, k & 1, stn, kfrag[(t + 1) & 1], lane);
+        slot = (slot + 1 == D) ? 0 : slot + 1;
+      }
+      // copies into the ring past the last tile may still be landing
+      wait_vmcnt<0>();
 
-    // ---- epilogue: (m, l) of every vector from its QK wave to the PV waves
-    if (qk) {
-      const float l_tot = wave_sum_groups(l_part);
-      if (h4 == 0) ml_s[wave][n16] = make_float2(m_ref, l_tot);
-    }
-    __syncthreads();
+      // ---- epilogue: (m, l) of every vector from its QK wave to the PV waves
+      if (decltype(do_qk)::value && qk) {
+        const float l_tot = wave_sum_groups(l_part);
+        if (h4 == 0) ml_s[wave][n16] = make_float2(m_ref, l_tot);
+      }
+      __syncthreads();
 #pragma unroll
-    for (int jb = 0; jb < BPW; ++jb) {
-      const int b = R::block(wave, jb);
-      if (b >= NB) continue;
+      for (int jb = 0; jb < NBL; ++jb) {
+        const int b = R::block(wave, jb);
+        if (b >= NB) continue;
 #pragma unroll
-      for (int i = 0; i < NQW; ++i) {
-        const int n = q0 + GW * i;
-        const int vv = n * 16 + n16;
-        if (n >= nq || vv >= M) continue;
-        const int orow = r0 + vv / a.G;
-        const int ohead = g * a.G + vv % a.G;
-        const float2 ml = ml_s[n][n16];
-        const int dim0 = 32 * b + 4 * h4;
-        if (FINAL) {
-          const float inv_l = 1.0f / ml.y;
-          float* dst = a.out + ((size_t)orow * a.Hq + ohead) * HD + dim0;
-          *(float4_t*)dst = OR(jb, i, 0) * inv_l;
-          *(float4_t*)(dst + 16) = OR(jb, i, 1) * inv_l;
-        } else {
-          const size_t idx = ((size_t)split * a.n_rows + orow) * a.Hq + ohead;
-          float* dst = a.part_o + idx * HD + dim0;
-          *(float4_t*)dst = OR(jb, i, 0);
-          *(float4_t*)(dst + 16) = OR(jb, i, 1);
-          if (b == 0 && h4 == 0) a.part_ml[idx] = ml;
+        for (int i = 0; i < NQW; ++i) {
+          const int n = q0 + GW * i;
+          const int vv = n * 16 + n16;
+          if (n >= nq || vv >= M) continue;
+          const int orow = r0 + vv / a.G;
+          const int ohead = g * a.G + vv % a.G;
+          const float2 ml = ml_s[n][n16];
+          const int dim0 = 32 * b + 4 * h4;
+          if (FINAL) {
+            const float inv_l = 1.0f / ml.y;
+            float* dst = a.out + ((size_t)orow * a.Hq + ohead) * HD + dim0;
+            *(float4_t*)dst = Oa[jb][i][0] * inv_l;
+            *(float4_t*)(dst + 16) = Oa[jb][i][1] * inv_l;
+          } else {
+            const size_t idx = ((size_t)split * a.n_rows + orow) * a.Hq + ohead;
+            float* dst = a.part_o + idx * HD + dim0;
+            *(float4_t*)dst = Oa[jb][i][0];
+            *(float4_t*)(dst + 16) = Oa[jb][i][1];
+            if (b == 0 && h4 == 0) a.part_ml[idx] = ml;
+          }
         }
       }
+    };
+    using T_ = std::true_type;
+    using F_ = std::false_type;
+    if constexpr (R::UNEVEN) {
+      if (wave < 2) {
+        float4_t Oa[1][NQW][2];  // (no blocks: never multiplied)
+        role_loop(T_(), T_(), Oa);
+      } else if (wave < 6) {
+        float4_t Oa[1][NQW][2];
+        role_loop(T_(), F_(), Oa);
+      } else {
+        float4_t Oa[2][NQW][2];
+        role_loop(F_(), F_(), Oa);
+      }
+    } else {
+      float4_t Oa[BPW][NQW][2];
+      role_loop(T_(), T_(), Oa);
     }
   }
 #undef QR
-#undef OR
 }
 
 // Merge split partials: one 256-thread workgroup per (row, Q head, 64-dim

@@ -45,10 +45,10 @@ int launch_status() {
 
 // Vector-tile capacity of the kernel instance for a row group of `vectors`
 // query vectors (16 per tile): the smallest instance that holds them (at
-// head_dim 128 and 64 the instances below 8 hold 2 or 4 and 4 tiles).
+// head_dim 256: 2, 3, 4, 6 or 8 tiles; at 128: 2, 4 or 8; at 64: 4 or 8).
 int nq_for(int vectors, int hd) {
   const int n = (vectors + 15) / 16;
-  if (n > 4) return 8;
+  if (n > 4) return (n <= 6 && hd == 256) ? 6 : 8;
   if (hd == 256) return n <= 2 ? 2 : n;
   if (hd == 128) return n <= 2 ? 2 : 4;
   return 4;
@@ -85,6 +85,7 @@ KernelFn pick_nq(int nq) {
     case 2: if constexpr (HD >= 128) return attend_q8_kernel<HD, QF32, FINAL, 2>; else return nullptr;
     case 3: if constexpr (HD == 256) return attend_q8_kernel<HD, QF32, FINAL, 3>; else return nullptr;
     case 4: return attend_q8_kernel<HD, QF32, FINAL, 4>;
+    case 6: if constexpr (HD == 256) return attend_q8_kernel<HD, QF32, FINAL, 6>; else return nullptr;
     case 8: return attend_q8_kernel<HD, QF32, FINAL, 8>;
     default: return nullptr;
   }
