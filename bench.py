@@ -13,6 +13,12 @@ launches are queued so that host submission latency does not enter them.
 Prints one JSON line.  Other modes:
   --copy-calibration   run only plain device copies of a known size (for
                        scaling the FETCH_SIZE / WRITE_SIZE counters)
+  --sweep              the shared-scan comparison over context lengths: the
+                       verify call (8 rows) with one row per workgroup (every
+                       row scans K/V on its own) against row groups of 4 and 8
+                       rows, at 24 Q / 4 KV heads, head_dim 256, contexts
+                       2,048 / 4,096 / 20,676 / 32,768 and head_dim 128 at
+                       8,192; one JSON line per cell
 """
 
 from __future__ import annotations
@@ -49,6 +55,7 @@ def parse():
     ap.add_argument("--splits", type=int, default=0)
     ap.add_argument("--rotate-bytes", type=float, default=1.1e9)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--sweep", action="store_true")
     return ap.parse_args()
 
 
@@ -99,6 +106,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.sweep:
+        sweep(args)
         return
 
     import torch
@@ -301,6 +311,96 @@ def cpu_baseline(wv, iv):
         "sample": f"{wv.name}: KV head 0 with its {wv.group} Q heads x {wv.n_rows} rows "
                   f"({sample_bytes} KV bytes), {reps} repetitions of {dt:.3f} s",
     }
+
+
+# The context sweep of "perf(gfx1100): share Q8 KV scans across verifier rows",
+# Kernel evidence: (n_q_heads, n_kv_heads, head_dim, ctx).  The page gives the
+# head_dim 128 screen without its head counts; it is taken at the same 24 / 4.
+SWEEP_SHAPES = [(24, 4, 256, 2048), (24, 4, 256, 4096), (24, 4, 256, 20676),
+                (24, 4, 256, 32768), (24, 4, 128, 8192)]
+SWEEP_ROWS = 8
+SWEEP_GROUPS = (1, 4, 8)
+
+
+def time_verify(ops, bufs, w, rows_per_group, steps, warmup):
+    """Mean kernel and reducer durations (s) of the verify call over rotating inputs."""
+    import torch
+
+    S = ops.verify_splits(w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx_len, w.n_rows,
+                          rows_per_group)
+    ws = torch.empty(ops.workspace_bytes(w.n_rows, w.n_q_heads, w.head_dim, S),
+                     dtype=torch.uint8, device=bufs[0][0].device)
+    out = torch.empty((w.n_rows, w.n_q_heads, w.head_dim), dtype=torch.float32,
+                      device=ws.device)
+
+    def call(i):
+        q, kc, ks, vc, vs = bufs[i % len(bufs)]
+        ops.verify_partials(q, kc, ks, vc, vs, ctx_len=w.ctx_len,
+                            rows_per_group=rows_per_group, n_splits=S, workspace=ws)
+
+    def reduce():
+        ops.reduce_partials(ws, w.n_rows, w.n_q_heads, w.head_dim, S, out=out)
+
+    for i in range(warmup):
+        call(i)
+        reduce()
+    call(0)
+    path = ops.last_path()
+    torch.cuda.synchronize()
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ev = [[E() for _ in range(3)] for _ in range(steps)]
+    torch.cuda._sleep(int(2.4e9 * (0.05e-3 * steps + 0.02)))
+    for i in range(steps):
+        ev[i][0].record()
+        call(i + 1)
+        ev[i][1].record()
+        reduce()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    k1 = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e-3
+    k2 = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e-3
+    return k1, k2, S, path
+
+
+def sweep(args):
+    import torch
+
+    import workloads as W
+    from attention_int8_quantized_amd import ops
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    steps = min(args.steps, 30)
+    for hq, hkv, hd, ctx in SWEEP_SHAPES:
+        w = W.VerifyWorkload(f"sweep_hd{hd}_ctx{ctx}", hq, hkv, hd, ctx, SWEEP_ROWS, SWEEP_ROWS)
+        inp = W.generate(w)
+        host = [inp.q, inp.k_codes, inp.k_scales, inp.v_codes, inp.v_scales]
+        kv_bytes = sum(x.nbytes for x in host[1:])
+        n = max(1, min(256, int(args.rotate_bytes // kv_bytes) + 1))
+        base = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in host]
+        bufs = [base] + [[t.clone() for t in base] for _ in range(n - 1)]
+        torch.cuda.synchronize()
+        cells = {}
+        for rg in SWEEP_GROUPS:
+            k1, k2, S, path = time_verify(ops, bufs, w, rg, steps, args.warmup)
+            cells[rg] = (k1, k2, S, path)
+        t1 = cells[1][0] + cells[1][1]
+        for rg in SWEEP_GROUPS:
+            k1, k2, S, path = cells[rg]
+            tot = k1 + k2
+            line = {
+                "mode": "sweep", "n_q_heads": hq, "n_kv_heads": hkv, "head_dim": hd,
+                "ctx": ctx, "rows": SWEEP_ROWS, "rows_per_group": rg, "splits": S,
+                "path": path, "kernel_us": round(k1 * 1e6, 3), "reduce_us": round(k2 * 1e6, 3),
+                "total_us": round(tot * 1e6, 3),
+                "visible_kv_gbs": round(w.visible_kv_bytes(rg) / tot / 1e9, 1),
+                "unique_kv_gbs": round(w.unique_kv_bytes() / tot / 1e9, 1),
+                "speedup_vs_rows_per_group_1": round(t1 / tot, 3),
+                "rotating_copies": n, "steps": steps,
+            }
+            print(json.dumps(line), flush=True)
+        del bufs, base
+        torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

@@ -39,7 +39,9 @@ def test_i8_to_f16_all_byte_pairs():
 @pytest.mark.parametrize("name,rg", [
     ("tiny_verify", 0),
     ("verify_window", 0),
+    ("verify_window", 1),
     ("verify_batch", 4),
+    ("verify_batch", 1),
     ("verify_batch", 0),
     ("long_verify", 0),
 ])
