@@ -1,4 +1,4 @@
-"""CPU reference for int8-KV GQA attention.
+"""CPU reference for int8-KV GQA attention and for the KV append quantiser.
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, ``__graft_entry__.smoke()``
 and the ``cpu_baseline`` leg of ``bench.py``; never by the library.
@@ -14,3 +14,4 @@ from .core import (  # noqa: F401
     split_partials,
     verify,
 )
+from .quant import kv_append, quantize_q8  # noqa: F401
