@@ -44,6 +44,10 @@ _SIGNATURES = {
         [_vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
          _c_float, _vp, _vp],
     ),
+    "attn_kv_append_q8": (
+        _c_int,
+        [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_int, _vp],
+    ),
     "attnq8_selftest_i8_to_f16": (_c_int, [_vp, _vp]),
     "attnq8_status_string": (ctypes.c_char_p, [_c_int]),
     "attnq8_last_path": (ctypes.c_char_p, []),

@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include "../../include/attnq8.h"
+#include "append_kernel.h"
 #include "attend_kernel.h"
 
 namespace {
@@ -17,6 +18,8 @@ using namespace attnq8;
 constexpr int kMaxVectorsPerGroup = 128;  // query vectors of one row group
 constexpr int kTargetCUs = 256;           // MI355X compute units
 constexpr double kLog2e = 1.4426950408889634;
+constexpr int kMaxAppendHeadDim = 4096;   // KV append: any multiple of 32 up to this
+constexpr long long kAppendMaxBlocks = 8192;  // 32 workgroups per CU, then grid-stride
 
 thread_local char g_last_path[192] = "none";
 
@@ -288,6 +291,62 @@ int attn_prompt_q8(const void* q, int q_dtype, const int8_t* k_codes, const uint
   snprintf(g_last_path, sizeof(g_last_path),
            "prompt hd%d q%s tiles%d rows_per_group%d groups%d kv_heads%d", head_dim,
            q_dtype == ATTNQ8_F32 ? "f32" : "f16", nq, rq, groups, n_kv_heads);
+  return ATTNQ8_OK;
+}
+
+int attn_kv_append_q8(const void* k, const void* v, int x_dtype, int n_tokens, int n_kv_heads,
+                      int head_dim, int8_t* k_codes, uint16_t* k_scales, int8_t* v_codes,
+                      uint16_t* v_scales, int kv_stride, int pos0, void* stream) {
+  // the row pointers may be NULL only when there are no rows
+  const bool has_v = v || v_codes || v_scales;
+  if (!k_codes || !k_scales) return ATTNQ8_EINVAL;
+  if (has_v && (!v_codes || !v_scales)) return ATTNQ8_EINVAL;
+  if (n_tokens > 0 && (!k || (has_v && !v))) return ATTNQ8_EINVAL;
+  if (x_dtype != ATTNQ8_F32 && x_dtype != ATTNQ8_F16) return ATTNQ8_EINVAL;
+  if (n_tokens < 0 || n_kv_heads < 1 || kv_stride < 1 || pos0 < 0) return ATTNQ8_EINVAL;
+  if (head_dim < 32 || head_dim > kMaxAppendHeadDim || head_dim % 32) return ATTNQ8_EUNSUPPORTED;
+  if ((long long)pos0 + n_tokens > kv_stride) return ATTNQ8_EINVAL;
+  if (!aligned(k, 16) || !aligned(k_codes, 16) || !aligned(k_scales, 4)) return ATTNQ8_EALIGN;
+  if (has_v && (!aligned(v, 16) || !aligned(v_codes, 16) || !aligned(v_scales, 4)))
+    return ATTNQ8_EALIGN;
+  const long long row_units = (long long)n_kv_heads * head_dim / 8;
+  if (row_units > (1LL << 30)) return ATTNQ8_EINVAL;
+  const long long units = row_units * n_tokens;
+  if (units == 0) {
+    snprintf(g_last_path, sizeof(g_last_path), "kv_append empty");
+    return ATTNQ8_OK;
+  }
+  int st = device_status();
+  if (st) return st;
+  AppendArgs a;
+  a.x[0] = k;
+  a.x[1] = v;
+  a.codes[0] = k_codes;
+  a.codes[1] = v_codes;
+  a.scales[0] = k_scales;
+  a.scales[1] = v_scales;
+  a.units = units;
+  a.row_units = (int)row_units;
+  a.head_units = head_dim / 8;
+  a.head_dim = head_dim;
+  a.kv_stride = kv_stride;
+  a.pos0 = pos0;
+  long long blocks = (units + kAppendThreads - 1) / kAppendThreads;
+  if (blocks > kAppendMaxBlocks) blocks = kAppendMaxBlocks;
+  const long long step = blocks * kAppendThreads;
+  a.step_tokens = (int)(step / row_units);
+  a.step_in_row = (int)(step % row_units);
+  const dim3 grid((unsigned)blocks, has_v ? 2 : 1);
+  if (x_dtype == ATTNQ8_F32)
+    hipLaunchKernelGGL(kv_append_q8_kernel<true>, grid, dim3(kAppendThreads), 0,
+                       (hipStream_t)stream, a);
+  else
+    hipLaunchKernelGGL(kv_append_q8_kernel<false>, grid, dim3(kAppendThreads), 0,
+                       (hipStream_t)stream, a);
+  st = launch_status();
+  if (st) return st;
+  snprintf(g_last_path, sizeof(g_last_path), "kv_append hd%d x%s tensors%d blocks%lld units%lld",
+           head_dim, x_dtype == ATTNQ8_F32 ? "f32" : "f16", has_v ? 2 : 1, blocks, units);
   return ATTNQ8_OK;
 }
 

@@ -122,6 +122,37 @@ def prompt(q, k_codes, k_scales, v_codes, v_scales, q_pos0: int, kv_len: Optiona
     return out
 
 
+def kv_append(k: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, pos0: int,
+              v: Optional[torch.Tensor] = None, v_codes: Optional[torch.Tensor] = None,
+              v_scales: Optional[torch.Tensor] = None) -> None:
+    """Quantise rows k (and v) [n_tokens][Hkv][hd] into the cache at pos0 (in place)."""
+    pairs = [("k", k, k_codes, k_scales)]
+    if v is not None or v_codes is not None or v_scales is not None:
+        if v is None or v_codes is None or v_scales is None:
+            raise ValueError("v, v_codes and v_scales go together")
+        pairs.append(("v", v, v_codes, v_scales))
+    for name, x, c, s in pairs:
+        for n2, t in ((name, x), (name + "_codes", c), (name + "_scales", s)):
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError(f"{n2} must be a contiguous GPU tensor")
+        if x.dtype not in _QTYPES or c.dtype != torch.int8 or s.dtype != torch.float16:
+            raise ValueError(f"{name}: rows float32/float16, codes int8, scales float16")
+        if x.dim() != 3 or c.dim() != 3 or s.dim() != 3:
+            raise ValueError(f"{name}: rows [T][Hkv][hd], codes [Hkv][stride][hd], scales [Hkv][stride][hd/32]")
+        if x.shape[1] != c.shape[0] or x.shape[2] != c.shape[2] or \
+                s.shape != (c.shape[0], c.shape[1], c.shape[2] // 32):
+            raise ValueError(f"{name}: inconsistent shapes")
+    if len(pairs) == 2 and (v.shape != k.shape or v.dtype != k.dtype or v_codes.shape != k_codes.shape):
+        raise ValueError("k and v must match")
+    T, H, hd = k.shape
+    nul = 0
+    st = _lib.load().attn_kv_append_q8(
+        _ptr(k), _ptr(v) if v is not None else nul, _QTYPES[k.dtype], T, H, hd, _ptr(k_codes),
+        _ptr(k_scales), _ptr(v_codes) if v is not None else nul,
+        _ptr(v_scales) if v is not None else nul, k_codes.shape[1], pos0, _stream())
+    _lib.check("attn_kv_append_q8", st)
+
+
 def selftest_i8_to_f16(device="cuda") -> torch.Tensor:
     out = torch.empty(2 * 65536, dtype=torch.int16, device=device)
     _lib.check("attnq8_selftest_i8_to_f16",

@@ -50,6 +50,7 @@ def parse():
     ap.add_argument("--verify-workload", default="verify_window")
     ap.add_argument("--prompt-workload", default="prompt_chunk")
     ap.add_argument("--no-prompt", action="store_true")
+    ap.add_argument("--no-append", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rows-per-group", type=int, default=0)
     ap.add_argument("--splits", type=int, default=0)
@@ -272,6 +273,8 @@ def main():
             "traffic": load_traffic("prompt"),
         }
     res["host_wall_s"] = round(wall, 3)
+    if not args.no_append:
+        res["kv_append"] = time_append(ops, dev, min(K, 20), args.warmup)
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wv, iv)
@@ -310,6 +313,55 @@ def cpu_baseline(wv, iv):
         "kind": "oracle",
         "sample": f"{wv.name}: KV head 0 with its {wv.group} Q heads x {wv.n_rows} rows "
                   f"({sample_bytes} KV bytes), {reps} repetitions of {dt:.3f} s",
+    }
+
+
+# KV append measured beside the attention: the K and V rows of a 32,768-token
+# context, 4 KV heads, head_dim 256, fp32 rows in, int8 blocks + fp16 scales out.
+APPEND_SHAPE = (32768, 4, 256)
+
+
+def time_append(ops, dev, steps, warmup):
+    import torch
+
+    T, H, hd = APPEND_SHAPE
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    rows = [[torch.randn((T, H, hd), generator=g, device=dev) for _ in range(2)] for _ in range(2)]
+    kc = torch.empty((H, T, hd), dtype=torch.int8, device=dev)
+    vc = torch.empty_like(kc)
+    ks = torch.empty((H, T, hd // 32), dtype=torch.float16, device=dev)
+    vs = torch.empty_like(ks)
+
+    def call(i):
+        k, v = rows[i % 2]
+        ops.kv_append(k, kc, ks, 0, v, vc, vs)
+
+    for i in range(warmup):
+        call(i)
+    call(0)
+    path = ops.last_path()
+    torch.cuda.synchronize()
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ev = [(E(), E()) for _ in range(steps)]
+    torch.cuda._sleep(int(2.4e9 * (0.05e-3 * steps + 0.02)))
+    for i in range(steps):
+        ev[i][0].record()
+        call(i + 1)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    n = T * H * hd
+    moved = 2 * (n * 4 + n + (n // 32) * 2)  # K and V: fp32 rows read, codes + scales written
+    gbs = moved / t / 1e9
+    return {
+        "workload": f"K and V rows of {T} tokens x {H} KV heads x head_dim {hd}, fp32",
+        "path": path,
+        "us_per_call": round(t * 1e6, 3),
+        "bytes": moved,
+        "gbs": round(gbs, 1),
+        "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+        "steps": steps,
     }
 
 

@@ -130,6 +130,36 @@ int attn_prompt_q8(const void* q, int q_dtype,
                    float sm_scale, float* out, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * KV append: quantise n_tokens new K (and V) rows into the cache at positions
+ * pos0 .. pos0 + n_tokens - 1 of every KV head.  The format is the pages' Q8
+ * KV block ("perf(gfx1100): share Q8 KV scans across verifier rows", Summary;
+ * the Q8_0 block of "[Engine] perf(hip): optimize MTP draft, shared expert,
+ * and verify/sampler head kernels on RDNA4", Problem and result item 2 and
+ * Verification & Parity Evidence).  For each block of 32 consecutive head_dim
+ * elements of one (token, KV head) row:
+ *     scale = fp16(amax / 127)   amax = max |x|; fp32 divide, round to nearest
+ *                                even into fp16 (+inf above the fp16 range)
+ *     code  = clamp(round_half_away_from_zero(x / scale), -127, 127),
+ *             x / scale an fp32 divide by the stored scale; scale 0 -> codes 0
+ * The results are bit-exact (they equal the exactly rounded quotients).
+ *
+ * Layouts: k, v [n_tokens][n_kv_heads][head_dim] fp32 or fp16 (x_dtype), 16-byte
+ * aligned, finite values; the cache planes as for the attention calls (codes
+ * [n_kv_heads][kv_stride][head_dim] int8, 16-byte aligned; scales
+ * [n_kv_heads][kv_stride][head_dim/32] fp16 bit patterns, 4-byte aligned).
+ * Only the n_tokens positions of each head are written.  head_dim is any
+ * multiple of 32 up to 4096.  Pass v, v_codes and v_scales all NULL to
+ * quantise K alone.  n_tokens = 0 launches nothing (the row pointers may then
+ * be NULL; the cache pointers are still checked).  Requires pos0 >= 0 and
+ * pos0 + n_tokens <= kv_stride; the input rows must not overlap the cache.
+ * ------------------------------------------------------------------------- */
+int attn_kv_append_q8(const void* k, const void* v, int x_dtype,
+                      int n_tokens, int n_kv_heads, int head_dim,
+                      int8_t* k_codes, uint16_t* k_scales,
+                      int8_t* v_codes, uint16_t* v_scales,
+                      int kv_stride, int pos0, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Diagnostics.
  *
  * attnq8_selftest_i8_to_f16: run the device's int8 -> fp16 code conversion

@@ -134,6 +134,39 @@ def test_reduce_rejects_before_launch(lib):
     assert f(A, 100, 4, 4, 64, 2, A, None) == _lib.EWORKSPACE
 
 
+def _append(lib, **kw):
+    args = dict(k=A, v=A, dt=0, T=8, H=4, hd=256, kc=A, ks=A, vc=A, vs=A, stride=20684, pos0=20676,
+                stream=None)
+    args.update(kw)
+    return lib.attn_kv_append_q8(args["k"], args["v"], args["dt"], args["T"], args["H"], args["hd"],
+                                 args["kc"], args["ks"], args["vc"], args["vs"], args["stride"],
+                                 args["pos0"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), _lib.EINVAL),
+    (dict(kc=None), _lib.EINVAL),
+    (dict(vs=None), _lib.EINVAL),            # V given without its scales
+    (dict(v=None), _lib.EINVAL),             # V cache given without V rows
+    (dict(dt=2), _lib.EINVAL),
+    (dict(T=-1), _lib.EINVAL),
+    (dict(H=0), _lib.EINVAL),
+    (dict(pos0=-1), _lib.EINVAL),
+    (dict(pos0=20677), _lib.EINVAL),         # last row beyond the stride
+    (dict(hd=48), _lib.EUNSUPPORTED),
+    (dict(hd=8192), _lib.EUNSUPPORTED),
+    (dict(k=A + 8), _lib.EALIGN),
+    (dict(vc=A + 8), _lib.EALIGN),
+    (dict(ks=A + 2), _lib.EALIGN),
+    (dict(T=0), _lib.OK),                    # nothing to write: no launch, no HIP call
+    (dict(T=0, v=None, vc=None, vs=None), _lib.OK),
+    (dict(T=0, k=None, v=None), _lib.OK),    # empty rows may come as NULL
+    (dict(T=0, kc=None), _lib.EINVAL),
+])
+def test_kv_append_rejects_before_launch(lib, kw, status):
+    assert _append(lib, **kw) == status
+
+
 def test_selftest_rejects_null(lib):
     assert lib.attnq8_selftest_i8_to_f16(None, None) == _lib.EINVAL
 
