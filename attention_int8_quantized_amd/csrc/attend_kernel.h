@@ -344,8 +344,39 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
   const int t_end = (int)(((long long)(split + 1) * n_tiles) / a.n_splits);
   const int k_end = min(n_keys, t_end * 32);
 
-  // ---- start the copies first so that their latency overlaps the q setup;
-  // tile t is copied D-2 iterations ahead into ring stage t % D
+  // ---- QK role: vector tile `wave` (column n16 of its S^T tile)
+  const bool qk = wave < nq;  // wave-uniform
+  const int v = wave * 16 + n16;
+  const bool v_ok = qk && v < M;
+  const int vr = v_ok ? v / a.G : 0;
+  const int vh = v_ok ? g * a.G + (v - vr * a.G) : 0;
+
+  // ---- the q loads go out before the tile copies: the copies occupy this
+  // CU's share of HBM bandwidth for thousands of cycles, and q (an L2 hit for
+  // all but the first workgroup of a head) would otherwise return behind them
+  constexpr int QRAW = QF32 ? 2 * NB : NB;
+  float4_t qraw[QRAW];
+  const size_t qoff = ((size_t)(r0 + vr) * a.Hq + vh) * HD + 8 * h4;
+#pragma unroll
+  for (int k = 0; k < QRAW; ++k) qraw[k] = (float4_t){0, 0, 0, 0};
+  if (v_ok) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (QF32) {
+        const float4_t* p = (const float4_t*)((const float*)a.q + qoff + 32 * b);
+        qraw[2 * b] = p[0];
+        qraw[2 * b + 1] = p[1];
+      } else {
+        qraw[b] = *(const float4_t*)((const half_t*)a.q + qoff + 32 * b);
+      }
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- then the copies; tile t is copied D-2 iterations ahead into ring
+  // stage t % D
   const size_t head_rows = (size_t)g * a.kv_stride;
   constexpr int NWI = R::NWI;
   const bool copies = R::copy_index(wave) >= 0;  // wave-uniform
@@ -362,12 +393,6 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
       cp.issue(ring0 + s * L::BYTES, (t_begin + s) * 32, t_begin + s < t_end);
   }
 
-  // ---- QK role: vector tile `wave` (column n16 of its S^T tile)
-  const bool qk = wave < nq;  // wave-uniform
-  const int v = wave * 16 + n16;
-  const bool v_ok = qk && v < M;
-  const int vr = v_ok ? v / a.G : 0;
-  const int vh = v_ok ? g * a.G + (v - vr * a.G) : 0;
   const int lim = v_ok ? a.pos0 + r0 + vr : -1;  // last key this vector sees
   const int lim_eff = min(lim, k_end - 1);        // ... within this split
   // the smallest of those over the wave's vectors (wave-uniform): tiles that end
@@ -389,24 +414,16 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
   if (qk) {
     float qv[NB][8];
     float amax = 0.0f;
-    const size_t qoff = ((size_t)(r0 + vr) * a.Hq + vh) * HD + 8 * h4;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       if (QF32) {
-        float4_t x0 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
-        if (v_ok) {
-          const float4_t* p = (const float4_t*)((const float*)a.q + qoff + 32 * b);
-          x0 = p[0];
-          x1 = p[1];
-        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          qv[b][e] = x0[e];
-          qv[b][4 + e] = x1[e];
+          qv[b][e] = qraw[2 * b][e];
+          qv[b][4 + e] = qraw[2 * b + 1][e];
         }
       } else {
-        half8_t x = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (v_ok) x = *(const half8_t*)((const half_t*)a.q + qoff + 32 * b);
+        const half8_t x = __builtin_bit_cast(half8_t, qraw[b]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) qv[b][e] = (float)x[e];
       }
@@ -865,26 +882,13 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_partials_kernel(const f
   const int tid = threadIdx.x;
   const int lane = tid & 63;
 
-  float M = -INFINITY;
-  for (int s = tid; s < n_splits; s += kReduceThreads) {
-    const float2 ml = part_ml[(size_t)s * n_pairs + pair];
-    if (ml.y > 0.0f) M = fmaxf(M, ml.x);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  if (lane == 0) wmax[tid >> 6] = M;
-  __syncthreads();
-  M = wmax[0];
-#pragma unroll
-  for (int w = 1; w < NWAVE; ++w) M = fmaxf(M, wmax[w]);
-
+  // the first batch of partials is requested before the maximum is known (the
+  // loads do not depend on it), so the kernel makes one trip to memory, not two
   const int slot = tid / LPS;
   const int dl = tid % LPS;
-  float4_t acc = {0, 0, 0, 0};
-  float den = 0.0f;
-  for (int s0 = slot; s0 < n_splits; s0 += NSLOT * B) {
-    float2 ml[B];
-    float4_t o[B];
+  float2 ml[B];
+  float4_t o[B];
+  auto load_batch = [&](int s0) {
 #pragma unroll
     for (int i = 0; i < B; ++i) {
       const int sp = min(s0 + i * NSLOT, n_splits - 1);
@@ -892,6 +896,25 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_partials_kernel(const f
       ml[i] = part_ml[idx];
       o[i] = *(const float4_t*)(part_o + idx * HD + dim0 + 4 * dl);
     }
+  };
+  load_batch(slot);
+
+  float M = -INFINITY;
+  for (int s = tid; s < n_splits; s += kReduceThreads) {
+    const float2 m = part_ml[(size_t)s * n_pairs + pair];
+    if (m.y > 0.0f) M = fmaxf(M, m.x);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  if (lane == 0) wmax[tid >> 6] = M;
+  __syncthreads();
+  M = wmax[0];
+#pragma unroll
+  for (int w = 1; w < NWAVE; ++w) M = fmaxf(M, wmax[w]);
+
+  float4_t acc = {0, 0, 0, 0};
+  float den = 0.0f;
+  for (int s0 = slot;;) {
 #pragma unroll
     for (int i = 0; i < B; ++i) {
       if (s0 + i * NSLOT < n_splits) {
@@ -900,6 +923,9 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_partials_kernel(const f
         acc += w * o[i];
       }
     }
+    s0 += NSLOT * B;
+    if (s0 >= n_splits) break;
+    load_batch(s0);
   }
   slot_acc[slot][dl] = acc;
   if (dl == 0) slot_den[slot] = den;
