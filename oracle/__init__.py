@@ -1,4 +1,5 @@
-"""CPU reference for int8-KV GQA attention and for the KV append quantiser.
+"""CPU reference for int8-KV GQA attention, the KV append quantiser and the
+verify head's greedy token.
 
 TEST INFRASTRUCTURE ONLY: imported by the tests, ``__graft_entry__.smoke()``
 and the ``cpu_baseline`` leg of ``bench.py``; never by the library.
@@ -15,3 +16,4 @@ from .core import (  # noqa: F401
     verify,
 )
 from .quant import kv_append, quantize_q8  # noqa: F401
+from .head import greedy_head  # noqa: F401
