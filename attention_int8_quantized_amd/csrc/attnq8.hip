@@ -10,6 +10,7 @@
 #include "../../include/attnq8.h"
 #include "append_kernel.h"
 #include "attend_kernel.h"
+#include "head_kernel.h"
 
 namespace {
 
@@ -347,6 +348,52 @@ int attn_kv_append_q8(const void* k, const void* v, int x_dtype, int n_tokens, i
   if (st) return st;
   snprintf(g_last_path, sizeof(g_last_path), "kv_append hd%d x%s tensors%d blocks%lld units%lld",
            head_dim, x_dtype == ATTNQ8_F32 ? "f32" : "f16", has_v ? 2 : 1, blocks, units);
+  return ATTNQ8_OK;
+}
+
+// Blocks per row of the greedy head: about 2,048 blocks over all rows, at most
+// one 2,048-logit chunk per block, at most kHeadMaxBlocks.
+static int head_blocks_per_row(int n_rows, int vocab) {
+  const long long chunks = ((long long)vocab + kHeadChunk - 1) / kHeadChunk;
+  long long b = (2048 + n_rows - 1) / n_rows;
+  if (b > chunks) b = chunks;
+  if (b > kHeadMaxBlocks) b = kHeadMaxBlocks;
+  if (b < 1) b = 1;
+  return (int)b;
+}
+
+size_t attn_verify_head_workspace_bytes(int n_rows, int vocab) {
+  if (n_rows < 1 || n_rows > kHeadMaxRows || vocab < 1) return 0;
+  const int bpr = head_blocks_per_row(n_rows, vocab);
+  // the tickets first, at fixed offsets for every shape, then the block states
+  return kHeadTicketBytes + (size_t)n_rows * bpr * sizeof(HeadState);
+}
+
+int attn_verify_head_greedy(const float* logits, int n_rows, int vocab, long long row_stride,
+                            int* token, float* top_prob, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (!logits || !token || !workspace) return ATTNQ8_EINVAL;
+  if (n_rows < 1 || n_rows > kHeadMaxRows || vocab < 1 || row_stride < vocab) return ATTNQ8_EINVAL;
+  if (!aligned(logits, 4) || !aligned(token, 4) || !aligned(workspace, 16)) return ATTNQ8_EALIGN;
+  if (top_prob && !aligned(top_prob, 4)) return ATTNQ8_EALIGN;
+  if (workspace_bytes < attn_verify_head_workspace_bytes(n_rows, vocab)) return ATTNQ8_EWORKSPACE;
+  int st = device_status();
+  if (st) return st;
+  HeadArgs a;
+  a.logits = logits;
+  a.row_stride = row_stride;
+  a.vocab = vocab;
+  a.blocks_per_row = head_blocks_per_row(n_rows, vocab);
+  a.ticket = (unsigned*)workspace;
+  a.part = (HeadState*)((char*)workspace + kHeadTicketBytes);
+  a.token = token;
+  a.top_prob = top_prob;
+  hipLaunchKernelGGL(head_greedy_kernel, dim3(a.blocks_per_row, n_rows), dim3(kHeadThreads), 0,
+                     (hipStream_t)stream, a);
+  st = launch_status();
+  if (st) return st;
+  snprintf(g_last_path, sizeof(g_last_path), "verify_head rows%d vocab%d blocks_per_row%d", n_rows,
+           vocab, a.blocks_per_row);
   return ATTNQ8_OK;
 }
 

@@ -153,6 +153,37 @@ def kv_append(k: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, po
     _lib.check("attn_kv_append_q8", st)
 
 
+def head_workspace_bytes(n_rows: int, vocab: int) -> int:
+    return int(_lib.load().attn_verify_head_workspace_bytes(n_rows, vocab))
+
+
+def verify_head_greedy(logits: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                       token: Optional[torch.Tensor] = None,
+                       top_prob: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Greedy token (int32) and its probability (fp32) for each row of fp32 logits.
+
+    A workspace passed in must have been zero-filled before its first use; the
+    call leaves it ready for the next call.
+    """
+    if not logits.is_cuda or logits.dtype != torch.float32 or logits.dim() != 2:
+        raise ValueError("logits must be a float32 [rows][vocab] GPU tensor")
+    if logits.stride(1) != 1:
+        raise ValueError("logits rows must be contiguous")
+    rows, vocab = logits.shape
+    need = head_workspace_bytes(rows, vocab)
+    if workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=logits.device)
+    if token is None:
+        token = torch.empty(rows, dtype=torch.int32, device=logits.device)
+    if top_prob is None:
+        top_prob = torch.empty(rows, dtype=torch.float32, device=logits.device)
+    st = _lib.load().attn_verify_head_greedy(_ptr(logits), rows, vocab, logits.stride(0),
+                                             _ptr(token), _ptr(top_prob), _ptr(workspace),
+                                             workspace.numel(), _stream())
+    _lib.check("attn_verify_head_greedy", st)
+    return token, top_prob
+
+
 def selftest_i8_to_f16(device="cuda") -> torch.Tensor:
     out = torch.empty(2 * 65536, dtype=torch.int16, device=device)
     _lib.check("attnq8_selftest_i8_to_f16",

@@ -275,6 +275,7 @@ def main():
     res["host_wall_s"] = round(wall, 3)
     if not args.no_append:
         res["kv_append"] = time_append(ops, dev, min(K, 20), args.warmup)
+        res["verify_head"] = time_head(ops, dev, min(K, 20), args.warmup)
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wv, iv)
@@ -361,6 +362,52 @@ def time_append(ops, dev, steps, warmup):
         "bytes": moved,
         "gbs": round(gbs, 1),
         "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+        "steps": steps,
+    }
+
+
+# The verify head measured beside the attention: greedy token and top
+# probability of 5 rows of 248,320 fp32 logits (the sampler page's benchmark
+# shape), several rotating copies so that the rows come from HBM.
+HEAD_SHAPE = (5, 248320)
+
+
+def time_head(ops, dev, steps, warmup):
+    import torch
+
+    rows, V = HEAD_SHAPE
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    copies = [torch.randn((rows, V), generator=g, device=dev) * 3 for _ in range(64)]
+    ws = torch.zeros(ops.head_workspace_bytes(rows, V), dtype=torch.uint8, device=dev)
+    tok = torch.empty(rows, dtype=torch.int32, device=dev)
+    top = torch.empty(rows, dtype=torch.float32, device=dev)
+
+    def call(i):
+        ops.verify_head_greedy(copies[i % len(copies)], workspace=ws, token=tok, top_prob=top)
+
+    for i in range(warmup):
+        call(i)
+    call(0)
+    path = ops.last_path()
+    torch.cuda.synchronize()
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ev = [(E(), E()) for _ in range(steps)]
+    torch.cuda._sleep(int(2.4e9 * (0.05e-3 * steps + 0.02)))
+    for i in range(steps):
+        ev[i][0].record()
+        call(i + 1)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    moved = rows * V * 4
+    return {
+        "workload": f"{rows} rows x {V} fp32 logits: greedy token + top probability",
+        "path": path,
+        "us_per_call": round(t * 1e6, 3),
+        "bytes": moved,
+        "gbs": round(moved / t / 1e9, 1),
+        "frac_hbm": round(moved / t / 1e9 / HBM_PEAK_GBS, 4),
         "steps": steps,
     }
 

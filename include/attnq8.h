@@ -160,6 +160,35 @@ int attn_kv_append_q8(const void* k, const void* v, int x_dtype,
                       int kv_stride, int pos0, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Verify head: the greedy token and its probability for each row of logits
+ * ("[Engine] perf(hip): optimize MTP draft, shared expert, and verify/sampler
+ * head kernels on RDNA4", Problem and result item 1, Summary item 1 and
+ * Verification & Parity Evidence: T rows of 248,320 fp32 logits, ties, NaN
+ * and -inf entries, 1..8 rows on one scratch).  Per row x[0 .. vocab-1]:
+ *     token[r]    = the smallest i with x[i] = max of the non-NaN entries;
+ *                   -1 when every entry is NaN (-inf is an ordinary value)
+ *     top_prob[r] = 1 / sum_i exp(x[i] - x[token]) over the non-NaN entries
+ *                   (-inf entries add 0); NaN when no entry is finite
+ * +inf entries are outside the contract.  top_prob is computed in fp32 with a
+ * fixed merge order (run-to-run bitwise identical); its relative error is a
+ * few 1e-6.
+ *
+ * Layouts: logits fp32, row r at logits + r * row_stride (row_stride >= vocab,
+ * in elements; 4-byte alignment); token int32 [n_rows]; top_prob fp32
+ * [n_rows] or NULL.  The workspace (16-byte aligned, at least
+ * attn_verify_head_workspace_bytes(n_rows, vocab) bytes) holds one ticket per
+ * row at fixed offsets in its first 4,096 bytes, then per-block states: it
+ * must be zero-filled before its first use, and every completed call leaves
+ * the tickets at zero again, so one workspace (sized for the largest call)
+ * serves any sequence of calls of any shape on one stream.  Calls that share
+ * a workspace must not run concurrently.  1 <= n_rows <= 1024, vocab >= 1.
+ * ------------------------------------------------------------------------- */
+size_t attn_verify_head_workspace_bytes(int n_rows, int vocab);
+int attn_verify_head_greedy(const float* logits, int n_rows, int vocab,
+                            long long row_stride, int* token, float* top_prob,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Diagnostics.
  *
  * attnq8_selftest_i8_to_f16: run the device's int8 -> fp16 code conversion

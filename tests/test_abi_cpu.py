@@ -167,6 +167,43 @@ def test_kv_append_rejects_before_launch(lib, kw, status):
     assert _append(lib, **kw) == status
 
 
+def test_head_workspace_bytes(lib):
+    f = lib.attn_verify_head_workspace_bytes
+    # 4,096 bytes of tickets, then 16 bytes per block; 248,320 logits = 122
+    # chunks of 2,048: one chunk per block for 1..16 rows
+    assert f(1, 248320) == 4096 + 122 * 16
+    assert f(5, 248320) == 4096 + 5 * 122 * 16
+    assert f(64, 248320) == 4096 + 64 * 32 * 16   # 2,048 blocks over all rows
+    assert f(1, 1) == 4096 + 16
+    assert f(0, 100) == 0 and f(3, 0) == 0 and f(1025, 100) == 0
+
+
+def _head(lib, **kw):
+    args = dict(x=A, rows=5, V=248320, stride=248320, tok=A, top=A, ws=A, ws_bytes=1 << 20,
+                stream=None)
+    args.update(kw)
+    return lib.attn_verify_head_greedy(args["x"], args["rows"], args["V"], args["stride"],
+                                       args["tok"], args["top"], args["ws"], args["ws_bytes"],
+                                       args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), _lib.EINVAL),
+    (dict(tok=None), _lib.EINVAL),
+    (dict(ws=None), _lib.EINVAL),
+    (dict(rows=0), _lib.EINVAL),
+    (dict(rows=1025), _lib.EINVAL),
+    (dict(V=0), _lib.EINVAL),
+    (dict(stride=248319), _lib.EINVAL),
+    (dict(x=A + 2), _lib.EALIGN),
+    (dict(ws=A + 4), _lib.EALIGN),
+    (dict(top=A + 1), _lib.EALIGN),
+    (dict(ws_bytes=100), _lib.EWORKSPACE),
+])
+def test_head_rejects_before_launch(lib, kw, status):
+    assert _head(lib, **kw) == status
+
+
 def test_selftest_rejects_null(lib):
     assert lib.attnq8_selftest_i8_to_f16(None, None) == _lib.EINVAL
 
