@@ -80,17 +80,11 @@ def _masked_rows(qrows: np.ndarray, pos: np.ndarray, khat: np.ndarray,
     return out
 
 
-def attention(q: np.ndarray, positions: Sequence[int], k_codes, k_scales, v_codes,
-              v_scales, sm_scale: Optional[float] = None,
-              rows: Optional[Sequence[int]] = None) -> np.ndarray:
-    """Causal GQA attention of q [n][Hq][hd] rows at the given positions.
-
-    Returns fp64 [n][Hq][hd], or [len(rows)][Hq][hd] when a subset of row
-    indices is given.
-    """
+def _attend(q: np.ndarray, positions: Sequence[int], values_of, hkv: int,
+            sm_scale: Optional[float], rows: Optional[Sequence[int]]) -> np.ndarray:
+    """Causal GQA attention; values_of(g, T) gives KV head g's (Khat, Vhat) for keys 0..T-1."""
     q = np.asarray(q)
     n, hq, hd = q.shape
-    hkv = k_codes.shape[0]
     if hq % hkv:
         raise ValueError("n_q_heads must be a multiple of n_kv_heads")
     pos = np.asarray(positions, dtype=np.int64)
@@ -102,12 +96,41 @@ def attention(q: np.ndarray, positions: Sequence[int], k_codes, k_scales, v_code
     T = int(pos[sel].max()) + 1
     for g in range(hkv):
         heads = [h for h in range(hq) if kv_head_of(h, hq, hkv) == g]
-        khat = dequantize(k_codes[g, :T], k_scales[g, :T])
-        vhat = dequantize(v_codes[g, :T], v_scales[g, :T])
+        khat, vhat = values_of(g, T)
         for h in heads:
             qrows = q[sel, h, :].astype(np.float64)
             out[:, h, :] = _masked_rows(qrows, pos[sel], khat, vhat, scale)
     return out
+
+
+def attention(q: np.ndarray, positions: Sequence[int], k_codes, k_scales, v_codes,
+              v_scales, sm_scale: Optional[float] = None,
+              rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Causal GQA attention of q [n][Hq][hd] rows at the given positions.
+
+    Returns fp64 [n][Hq][hd], or [len(rows)][Hq][hd] when a subset of row
+    indices is given.
+    """
+    return _attend(q, positions,
+                   lambda g, T: (dequantize(k_codes[g, :T], k_scales[g, :T]),
+                                 dequantize(v_codes[g, :T], v_scales[g, :T])),
+                   np.asarray(k_codes).shape[0], sm_scale, rows)
+
+
+def attention_values(q: np.ndarray, positions: Sequence[int], khat, vhat,
+                     sm_scale: Optional[float] = None,
+                     rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """The same attention over K/V values given directly: khat, vhat [Hkv][T][hd].
+
+    An fp16 cache ("hip: gfx12 (RDNA4) WMMA kernel for the int8-KV QSA prompt
+    attention", What: fp16 KV pools) has Khat = K and Vhat = V; the values are
+    widened to fp64 exactly.
+    """
+    khat = np.asarray(khat)
+    vhat = np.asarray(vhat)
+    return _attend(q, positions,
+                   lambda g, T: (khat[g, :T].astype(np.float64), vhat[g, :T].astype(np.float64)),
+                   khat.shape[0], sm_scale, rows)
 
 
 def verify(q, k_codes, k_scales, v_codes, v_scales, ctx_len: int,
@@ -124,6 +147,27 @@ def prompt(q, k_codes, k_scales, v_codes, v_scales, q_pos0: int,
     n = np.asarray(q).shape[0]
     return attention(q, q_pos0 + np.arange(n), k_codes, k_scales, v_codes, v_scales,
                      sm_scale, rows)
+
+
+def _fp16(x):
+    x = np.asarray(x)
+    if x.dtype != np.float16:
+        raise TypeError("an fp16 cache holds float16 values")
+    return x
+
+
+def verify_f16kv(q, k, v, ctx_len: int, sm_scale: Optional[float] = None,
+                 rows=None) -> np.ndarray:
+    """Verify rows over an fp16 cache k, v [Hkv][stride][hd]."""
+    n = np.asarray(q).shape[0]
+    return attention_values(q, ctx_len + np.arange(n), _fp16(k), _fp16(v), sm_scale, rows)
+
+
+def prompt_f16kv(q, k, v, q_pos0: int, sm_scale: Optional[float] = None,
+                 rows=None) -> np.ndarray:
+    """Prompt chunk over an fp16 cache k, v [Hkv][stride][hd]."""
+    n = np.asarray(q).shape[0]
+    return attention_values(q, q_pos0 + np.arange(n), _fp16(k), _fp16(v), sm_scale, rows)
 
 
 # ----------------------------------------------------------------------------

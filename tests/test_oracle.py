@@ -73,3 +73,42 @@ def test_sm_scale_argument():
     got = oracle.attention(q, [1], kc, ks, vc, vs, sm_scale=0.3)
     D = 2.0 * 10 * 0.5 * 0.3
     assert abs(got[0, 0, 0] - math.exp(D) / (1 + math.exp(D))) < 1e-15
+
+
+# ---- the fp16-cache entry of the oracle (values given directly) ----------------
+
+
+def _attn_values(q, pos, kc, ks, vc, vs, sm_scale=None):
+    # the pins hand over int8 blocks; the values core receives them dequantised
+    # by the pins' own helper
+    return oracle.attention_values(q, pos, pins.deq(kc, ks), pins.deq(vc, vs), sm_scale)
+
+
+@pytest.mark.parametrize("check", pins.ATTENTION_CHECKS, ids=lambda f: f.__name__)
+def test_values_core_pin(check):
+    check(_attn_values)
+
+
+def test_values_core_equals_quantised_path_bitwise():
+    q, kc, ks, vc, vs = pins.random_case(61, 5, 8, 2, 64, 90)
+    pos = np.array([3, 40, 41, 88, 89])
+    a = oracle.attention(q, pos, kc, ks, vc, vs)
+    b = oracle.attention_values(q, pos, oracle.dequantize(kc, ks), oracle.dequantize(vc, vs))
+    assert np.array_equal(a, b)
+
+
+def test_f16kv_against_brute_force():
+    import bruteforce
+
+    rng = np.random.default_rng(62)
+    for hq, hkv, hd, T, n in ((4, 2, 32, 9, 3), (3, 1, 64, 20, 2), (2, 2, 32, 1, 1)):
+        k = rng.standard_normal((hkv, T, hd)).astype(np.float16)
+        v = (rng.standard_normal((hkv, T, hd)) * 4).astype(np.float16)
+        q = rng.standard_normal((n, hq, hd)).astype(np.float32)
+        ctx = T - n
+        got = oracle.verify_f16kv(q, k, v, ctx)
+        ones = np.ones((hkv, T, hd // 32))
+        ref = np.array(bruteforce.attention(q, ctx + np.arange(n), k, ones, v, ones))
+        assert np.max(np.abs(got - ref)) <= 1e-12 * np.abs(ref).max()
+        with pytest.raises(TypeError):
+            oracle.verify_f16kv(q, k.astype(np.float32), v, ctx)
