@@ -44,6 +44,16 @@ _SIGNATURES = {
         [_vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
          _c_float, _vp, _vp],
     ),
+    "attn_verify_f16kv": (
+        _c_int,
+        [_vp, _c_int, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+         _vp, _c_size, _c_float, _vp],
+    ),
+    "attn_prompt_f16kv": (
+        _c_int,
+        [_vp, _c_int, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_float,
+         _vp, _vp],
+    ),
     "attn_kv_append_q8": (
         _c_int,
         [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_int, _vp],

@@ -82,6 +82,7 @@ constexpr int kCopyLead = 3;  // tiles in flight ahead of the one being converte
 template <int HD>
 struct Stage {
   static constexpr int NB = HD / 32;
+  static constexpr int ROW = HD;                              // bytes per key row of a plane
   static constexpr int K_OFF = 0;
   static constexpr int V_OFF = 32 * HD;
   static constexpr int KS_OFF = 64 * HD;
@@ -92,6 +93,7 @@ struct Stage {
   static constexpr int NOPS = 2 * CODE_OPS + 2 * SCALE_OPS;   // copies per tile
   static constexpr int C = HD / 16;                           // 16-byte chunks per key row
   static constexpr int R = 16 / C;                            // key rows per 256 bytes
+  __device__ static int slot(int key, int c);
 };
 
 // MFMA fragments, 64 lanes x 16 B = 1 KB each:
@@ -113,7 +115,37 @@ __device__ __forceinline__ int chunk_slot(int key, int c) {
   return c ^ (((key / R) ^ ((key >> 4) * (C / 2))) & (C - 1));
 }
 
+template <int HD>
+__device__ __forceinline__ int Stage<HD>::slot(int key, int c) { return chunk_slot<HD>(key, c); }
+
 __device__ __forceinline__ int pi_key(int h, int e) { return (e < 4) ? 4 * h + e : 16 + 4 * h + (e - 4); }
+
+// LDS layout of one 32-key ring stage of an fp16 cache (bytes):
+//   K  [32 keys][HD] fp16, 16-byte chunks of a row permuted by slot()
+//   V  [32 keys][HD] fp16, same permutation
+// slot(key, c) = c ^ f(key) is an involution in c.  With 512- or 256-byte rows
+// (head_dim 256, 128) a row starts on the same bank group, and f takes 16
+// distinct values over any 16 consecutive keys (the K fragment reads) and 8
+// distinct slots over the 4 keys x 2 chunks of a transposing V read; with
+// 128-byte rows (head_dim 64) f spreads 16 consecutive keys over both halves of
+// the 256-byte bank cycle.
+template <int HD>
+struct Stage16 {
+  static constexpr int NB = HD / 32;
+  static constexpr int ROW = 2 * HD;
+  static constexpr int K_OFF = 0;
+  static constexpr int V_OFF = 64 * HD;
+  static constexpr int KS_OFF = 0;  // no scale planes
+  static constexpr int VS_OFF = 0;
+  static constexpr int BYTES = 128 * HD;
+  static constexpr int CODE_OPS = HD / 16;  // 1 KB copies per plane
+  static constexpr int SCALE_OPS = 0;
+  static constexpr int C = HD / 8;          // 16-byte chunks per key row
+  __device__ static int slot(int key, int c) {
+    if constexpr (C >= 16) return c ^ (2 * (key & 7) + ((key >> 3) & 1));
+    else return c ^ ((key >> 1) & (C - 1));
+  }
+};
 
 // The workgroup's direct-to-LDS copies of one 32-key tile, split over NW of its
 // waves.  A tile is CODE_OPS 1 KB copies of K codes, the same of V codes (the
@@ -124,9 +156,9 @@ __device__ __forceinline__ int pi_key(int h, int e) { return (e < 4) ? 4 * h + e
 // scale copies go one per wave to the waves after those (or from wave 0 when
 // every wave copies codes).  Offsets are computed once; per tile only the key
 // offset is added.
-template <int HD, int NW>
+template <class L, int NW>
 struct TileCopier {
-  using L = Stage<HD>;
+  static constexpr int HD = L::NB * 32;
   static constexpr bool WIDE = L::CODE_OPS >= NW;
   static constexpr int CPW = WIDE ? L::CODE_OPS / NW : 1;  // code chunks per copying wave
   static constexpr int NS = 2 * L::SCALE_OPS;              // scale copies per tile
@@ -149,16 +181,21 @@ struct TileCopier {
     for (int r = 0; r < CPW; ++r) {
       const int j = WIDE ? w + NW * r : w;  // chunk index within a plane
       const int pos = j * 1024 + 16 * lane;
-      const int row = pos / HD;
-      code_off[r] = row * HD + 16 * chunk_slot<HD>(row, (pos % HD) / 16);
+      const int row = pos / L::ROW;
+      code_off[r] = row * L::ROW + 16 * L::slot(row, (pos % L::ROW) / 16);
       code_lds[r] = j * 1024;
     }
     s_op = w - (WIDE ? 0 : L::CODE_OPS);
     if (s_op >= NS) s_op = -1;
-    const int jj = s_op % L::SCALE_OPS;
-    const int byte = jj * 256 + 4 * lane;
-    s_off = byte < 2 * HD ? byte : -1;
-    s_lds = (s_op >= L::SCALE_OPS ? L::VS_OFF : L::KS_OFF) + jj * 256;
+    if constexpr (L::SCALE_OPS > 0) {
+      const int jj = s_op % L::SCALE_OPS;
+      const int byte = jj * 256 + 4 * lane;
+      s_off = byte < 2 * HD ? byte : -1;
+      s_lds = (s_op >= L::SCALE_OPS ? L::VS_OFF : L::KS_OFF) + jj * 256;
+    } else {
+      s_off = -1;
+      s_lds = 0;
+    }
   }
 
   // copies per tile issued by this wave
@@ -171,15 +208,17 @@ struct TileCopier {
     if (codes) {
 #pragma unroll
       for (int r = 0; r < CPW; ++r) {
-        const int off = k0 * HD + code_off[r];
+        const int off = k0 * L::ROW + code_off[r];
         dma_b128(kc, lds + L::K_OFF + code_lds[r], off);
         dma_b128(vc, lds + L::V_OFF + code_lds[r], off);
       }
     }
-    if (s_op >= 0 && s_off >= 0) {
-      const int off = k0 * 2 * L::NB + s_off;
-      if (s_op < L::SCALE_OPS) dma_b32(ks, lds + s_lds, off);
-      else dma_b32(vs, lds + s_lds, off);
+    if constexpr (L::SCALE_OPS > 0) {
+      if (s_op >= 0 && s_off >= 0) {
+        const int off = k0 * 2 * L::NB + s_off;
+        if (s_op < L::SCALE_OPS) dma_b32(ks, lds + s_lds, off);
+        else dma_b32(vs, lds + s_lds, off);
+      }
     }
   }
 
@@ -247,6 +286,33 @@ __device__ __forceinline__ void convert_v(int b, const uint8_t* st, int lane, ha
   }
 }
 
+// V of block b (dim tiles 2b, 2b+1) of an fp16 ring stage -> V^T fragments
+// (exact: no lo part).  ds_read_b64_tr_b16: within a 16-lane group, lane j
+// receives element j % 4 of the 8-byte segments addressed by lanes j / 4 + 4i,
+// i = 0..3 (checked on the GPU with an in-bounds probe).  Lane q + 4i of group h
+// addresses key pi(h, i) (then pi(h, 4 + i)) at dims 16d + 4q, so that lane j
+// receives dim 16d + j of keys pi(h, 0..7): the same fragment as convert_v.
+template <int HD>
+__device__ __forceinline__ void read_v16(int b, const uint8_t* st, int lane, half8_t (&vh)[2]) {
+  using L = Stage16<HD>;
+  const int h4 = lane >> 4;
+  const int q = lane & 3;
+  const int i = (lane & 15) >> 2;
+#pragma unroll
+  for (int dd = 0; dd < 2; ++dd) {
+    const int c = 4 * b + 2 * dd + (q >> 1);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int key = pi_key(h4, 4 * half + i);
+      const uint8_t* p = st + L::V_OFF + key * L::ROW + 16 * L::slot(key, c) + 8 * (q & 1);
+      const half4_t v = __builtin_bit_cast(
+          half4_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)p));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vh[dd][4 * half + e] = v[e];
+    }
+  }
+}
+
 // Work split of a workgroup over its eight waves.  With at most four vector
 // tiles (NQ <= 4: verify row groups) the roles are disjoint: waves 0..3 own
 // one vector tile each for QK and do nothing else; waves 4..7 own the 32-dim
@@ -298,23 +364,30 @@ struct Roles {
 };
 
 // HD: head dim; QF32: q given in fp32 (else fp16); FINAL: write the normalised
-// output (else split partials); NQ: most 16-vector tiles per workgroup.
-template <int HD, bool QF32, bool FINAL, int NQ>
-__global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs a) {
-  using L = Stage<HD>;
+// output (else split partials); NQ: most 16-vector tiles per workgroup; KV16:
+// the cache holds fp16 K and V (no scales) instead of int8 blocks.
+template <int HD, bool QF32, bool FINAL, int NQ, bool KV16>
+__device__ __forceinline__ void attend_body(const AttendArgs& a) {
+  using L = std::conditional_t<KV16, Stage16<HD>, Stage<HD>>;
   using R = Roles<HD, NQ>;
   constexpr int NW = R::NW;
   constexpr int NB = L::NB;
   // ring stages: tiles t (QK, V), t+1 (K conversion) and the copies in
-  // flight, plus t-1 where PV converts V^T of its tile when it multiplies it
-  constexpr int LEAD = kCopyLead;
+  // flight, plus t-1 where PV converts V^T of its tile when it multiplies it.
+  // An fp16 stage is twice as large, so the prompt layout keeps one copy
+  // fewer in flight; with no K conversion a tile is needed only at its own
+  // iteration, so one more copy stays in flight at the barrier.
+  constexpr int LEAD = (KV16 && !R::SPLIT) ? kCopyLead - 1 : kCopyLead;
   constexpr int D = R::SPLIT ? LEAD + 1 : LEAD + 2;
+  constexpr int WAIT_NEWER = KV16 ? LEAD - 1 : LEAD - 2;
   constexpr int BPW = R::BPW;
   constexpr int GW = R::GW;
   constexpr int NQW = R::NQW;
-  constexpr int KF_BYTES = NB * 2 * 1024;
+  constexpr int KF_BYTES = KV16 ? 16 : NB * 2 * 1024;
   constexpr int PB_BYTES = NQ * 2 * 1024;
   static_assert(NQ <= NW, "one QK wave per vector tile");
+  static_assert(D * L::BYTES + 2 * KF_BYTES + 2 * PB_BYTES + 3 * NQ * 16 * 8 <= 160 * 1024,
+                "LDS per workgroup");
 
   __shared__ __attribute__((aligned(16))) uint8_t ring[D * L::BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t kfrag[2][KF_BYTES];
@@ -380,11 +453,13 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
   const size_t head_rows = (size_t)g * a.kv_stride;
   constexpr int NWI = R::NWI;
   const bool copies = R::copy_index(wave) >= 0;  // wave-uniform
-  TileCopier<HD, NWI> cp;
-  cp.kc = make_rsrc(a.kc + head_rows * HD, k_end * HD);
-  cp.vc = make_rsrc(a.vc + head_rows * HD, k_end * HD);
-  cp.ks = make_rsrc(a.ks + head_rows * NB, k_end * NB * 2);
-  cp.vs = make_rsrc(a.vs + head_rows * NB, k_end * NB * 2);
+  TileCopier<L, NWI> cp;
+  cp.kc = make_rsrc((const int8_t*)a.kc + head_rows * L::ROW, k_end * L::ROW);
+  cp.vc = make_rsrc((const int8_t*)a.vc + head_rows * L::ROW, k_end * L::ROW);
+  if constexpr (!KV16) {
+    cp.ks = make_rsrc(a.ks + head_rows * NB, k_end * NB * 2);
+    cp.vs = make_rsrc(a.vs + head_rows * NB, k_end * NB * 2);
+  }
   cp.init(copies ? R::copy_index(wave) : NWI, lane);
   const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
   if (copies) {
@@ -466,11 +541,13 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
   const int kw = R::k_workers(nq);
   const int ki = R::k_index(wave, nq);
 
-  // ---- prologue: K fragments of the first tile
-  if (t_begin < t_end) {
-    if (copies) cp.template wait_all_but<LEAD - 1>();
-    __syncthreads();
-    for (int k = wave; k < 2 * NB; k += NW) convert_k<HD>(k >> 1, k & 1, ring, kfrag[t_begin & 1], lane);
+  // ---- prologue: K fragments of the first tile (an fp16 cache is read in place)
+  if constexpr (!KV16) {
+    if (t_begin < t_end) {
+      if (copies) cp.template wait_all_but<LEAD - 1>();
+      __syncthreads();
+      for (int k = wave; k < 2 * NB; k += NW) convert_k<HD>(k >> 1, k & 1, ring, kfrag[t_begin & 1], lane);
+    }
   }
 
   // QK of tile t: S^T, mask, online softmax, P^T fragments and rescale factor
@@ -484,6 +561,28 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
     constexpr int KG = NB < 4 ? NB : (R::SPLIT || R::UNEVEN ? 2 : 4);  // blocks per group (registers)
     const half_t* Kst = (const half_t*)(st + L::KS_OFF);
     float4_t s[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+    if constexpr (KV16) {
+      // fp16 K fragments straight from the ring; no scales, so every block
+      // accumulates into the same S^T tile (in block order)
+#pragma unroll
+      for (int b0 = 0; b0 < NB; b0 += KG) {
+        half8_t kv[2][KG];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int j = 0; j < KG; ++j) {
+            const int key = 16 * u + n16;
+            kv[u][j] = *(const half8_t*)(st + L::K_OFF + key * L::ROW + 16 * L::slot(key, 4 * (b0 + j) + h4));
+          }
+#pragma unroll
+        for (int j = 0; j < KG; ++j)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            s[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv[u][j], QR(b0 + j), s[u], 0, 0, 0);
+            if (QF32) s[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv[u][j], QR(NB + b0 + j), s[u], 0, 0, 0);
+          }
+      }
+    } else {
 #pragma unroll
     for (int b0 = 0; b0 < NB; b0 += KG) {
       half8_t kv[2][KG];
@@ -518,6 +617,7 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
         for (int j = 0; j < KG; ++j)
 #pragma unroll
           for (int e = 0; e < 4; ++e) s[u][e] = fmaf((float)dk[u][e].get(j), acc[u][j][e], s[u][e]);
+    }
     }
     after_mfma();
     // mask and online softmax (base 2), p -> fp16 hi + lo
@@ -589,7 +689,10 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
     constexpr int PG = NBL > 1 ? 2 : (NQW < 4 ? NQW : 4);  // vector tiles per group (registers)
     half8_t vh[NBL][2], vl[NBL][2];
 #pragma unroll
-    for (int jb = 0; jb < NBL; ++jb) convert_v<HD>(R::block(wave, jb), st, lane, vh[jb], vl[jb]);
+    for (int jb = 0; jb < NBL; ++jb) {
+      if constexpr (KV16) read_v16<HD>(R::block(wave, jb), st, lane, vh[jb]);
+      else convert_v<HD>(R::block(wave, jb), st, lane, vh[jb], vl[jb]);
+    }
     const uint8_t* pf = pfrag[t & 1];
 #pragma unroll
     for (int i0 = 0; i0 < NQW; i0 += PG) {
@@ -621,11 +724,13 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
 #pragma unroll
             for (int dd = 0; dd < 2; ++dd)
               Oa[jb][i0 + j][dd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh[jb][dd], ph[j], Oa[jb][i0 + j][dd], 0, 0, 0);
+          if constexpr (!KV16) {
 #pragma unroll
-          for (int jb = 0; jb < NBL; ++jb)
+            for (int jb = 0; jb < NBL; ++jb)
 #pragma unroll
-            for (int dd = 0; dd < 2; ++dd)
-              Oa[jb][i0 + j][dd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl[jb][dd], ph[j], Oa[jb][i0 + j][dd], 0, 0, 0);
+              for (int dd = 0; dd < 2; ++dd)
+                Oa[jb][i0 + j][dd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vl[jb][dd], ph[j], Oa[jb][i0 + j][dd], 0, 0, 0);
+          }
 #pragma unroll
           for (int jb = 0; jb < NBL; ++jb)
 #pragma unroll
@@ -650,13 +755,15 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
         const uint8_t* stn = ring + ((slot + 1) % D) * L::BYTES;
         if (qk && t < t_end) {
           qk_tile(t, st, [] {});
-        } else if (ki == 0 && t + 1 < t_end) {
-          uint8_t* kfn = kfrag[(t + 1) & 1];
-          constexpr int KB = 2 * NB < 4 ? 2 * NB : 4;  // units per batch (registers)
+        } else if (!KV16 && ki == 0 && t + 1 < t_end) {
+          if constexpr (!KV16) {
+            uint8_t* kfn = kfrag[(t + 1) & 1];
+            constexpr int KB = 2 * NB < 4 ? 2 * NB : 4;  // units per batch (registers)
 #pragma unroll 1
-          for (int k0 = 0; k0 < 2 * NB; k0 += KB)
+            for (int k0 = 0; k0 < 2 * NB; k0 += KB)
 #pragma unroll
-            for (int j = 0; j < KB; ++j) convert_k<HD>((k0 + j) >> 1, (k0 + j) & 1, stn, kfn, lane);
+              for (int j = 0; j < KB; ++j) convert_k<HD>((k0 + j) >> 1, (k0 + j) & 1, stn, kfn, lane);
+          }
         }
         slot = (slot + 1 == D) ? 0 : slot + 1;
       }
@@ -678,24 +785,29 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
       int slot = 0;  // ring stage of tile t
       for (int t = t_begin; t <= t_end; ++t) {
         const bool has_qk = t < t_end;
-        if (t + 1 < t_end) cp.template wait_all_but<LEAD - 2>();  // this wave's copies of tile t+1 landed
+        // this wave's copies of tile t+1 (int8: K converted now) or t landed
+        if (KV16 ? has_qk : t + 1 < t_end) cp.template wait_all_but<WAIT_NEWER>();
         __syncthreads();  // K(t) converted; P(t-1) written; tile t+1 landed
         if (has_qk) cp.issue(ring0 + ((slot + LEAD) % D) * L::BYTES, (t + LEAD) * 32, t + LEAD < t_end);
         const uint8_t* st = ring + slot * L::BYTES;
         const uint8_t* stn = ring + ((slot + 1) % D) * L::BYTES;
         uint8_t* kfn = kfrag[(t + 1) & 1];
         auto kconv = [&]() {
-          if (kw == R::NPV) {
+          if (!KV16 && kw == R::NPV) {
 #pragma unroll
             for (int j = 0; j < (2 * NB + R::NPV - 1) / R::NPV; ++j) {
               const int k = ki + R::NPV * j;
-              if ((2 * NB) % R::NPV == 0 || k < 2 * NB) convert_k<HD>(k >> 1, k & 1, stn, kfn, lane);
+              if ((2 * NB) % R::NPV == 0 || k < 2 * NB)
+                if constexpr (!KV16) convert_k<HD>(k >> 1, k & 1, stn, kfn, lane);
             }
           }
         };
         half8_t vnh[BPW][2], vnl[BPW][2];
 #pragma unroll
-        for (int jb = 0; jb < BPW; ++jb) convert_v<HD>(R::block(wave, jb), st, lane, vnh[jb], vnl[jb]);
+        for (int jb = 0; jb < BPW; ++jb) {
+          if constexpr (KV16) read_v16<HD>(R::block(wave, jb), st, lane, vnh[jb]);
+          else convert_v<HD>(R::block(wave, jb), st, lane, vnh[jb], vnl[jb]);
+        }
         kconv();
         if (t > t_begin) {
           const uint8_t* pf = pfrag[(t - 1) & 1];
@@ -724,7 +836,8 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
                 }
             }
 #pragma unroll
-            for (int hl = 0; hl < 3; ++hl)
+            for (int hl = 0; hl < 3; ++hl) {
+              if (KV16 && hl == 1) continue;  // an fp16 V has no lo part
 #pragma unroll
               for (int j = 0; j < PG; ++j)
 #pragma unroll
@@ -733,6 +846,7 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
                   for (int dd = 0; dd < 2; ++dd)
                     O[jb][i0 + j][dd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                         hl == 1 ? vcl[jb][dd] : vch[jb][dd], hl == 2 ? pl[j] : ph[j], O[jb][i0 + j][dd], 0, 0, 0);
+            }
           }
         }
 #pragma unroll
@@ -740,7 +854,7 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
 #pragma unroll
           for (int dd = 0; dd < 2; ++dd) {
             vch[jb][dd] = vnh[jb][dd];
-            vcl[jb][dd] = vnl[jb][dd];
+            if constexpr (!KV16) vcl[jb][dd] = vnl[jb][dd];
           }
         slot = (slot + 1 == D) ? 0 : slot + 1;
       }
@@ -787,7 +901,8 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
       for (int t = t_begin; t <= t_end; ++t) {
         const bool has_qk = t < t_end;
         const bool has_next = t + 1 < t_end;
-        if (has_next) cp.template wait_all_but<LEAD - 2>();  // this wave's copies of tile t+1 landed
+        // this wave's copies of tile t+1 (int8: K converted now) or t landed
+        if (KV16 ? has_qk : has_next) cp.template wait_all_but<WAIT_NEWER>();
         __syncthreads();  // K(t) converted; P(t-1) written; tile t+1 landed; PV(t-2) done
         if (has_qk) cp.issue(ring0 + ((slot + LEAD) % D) * L::BYTES, (t + LEAD) * 32, t + LEAD < t_end);
         const uint8_t* st = ring + slot * L::BYTES;
@@ -795,8 +910,9 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
         const uint8_t* stn = ring + ((slot + 1) % D) * L::BYTES;
         if (decltype(do_qk)::value && qk && has_qk) qk_tile(t, st, [] {});
         if (nblk > 0 && t > t_begin) pv_tile(t - 1, st_prev, Oa);
-        if (decltype(do_k)::value && has_next)
-          for (int k = ki; k < 2 * NB; k += kw) convert_k<HD>(k >> 1, k & 1, stn, kfrag[(t + 1) & 1], lane);
+        if constexpr (!KV16 && decltype(do_k)::value)
+          if (has_next)
+            for (int k = ki; k < 2 * NB; k += kw) convert_k<HD>(k >> 1, k & 1, stn, kfrag[(t + 1) & 1], lane);
         slot = (slot + 1 == D) ? 0 : slot + 1;
       }
       // copies into the ring past the last tile may still be landing
@@ -855,6 +971,17 @@ __global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs
     }
   }
 #undef QR
+}
+
+template <int HD, bool QF32, bool FINAL, int NQ>
+__global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs a) {
+  attend_body<HD, QF32, FINAL, NQ, false>(a);
+}
+
+// The same attention over an fp16 K/V cache (no scales).
+template <int HD, bool QF32, bool FINAL, int NQ>
+__global__ __launch_bounds__(64 * kWaves) void attend_f16kv_kernel(const AttendArgs a) {
+  attend_body<HD, QF32, FINAL, NQ, true>(a);
 }
 
 // Merge split partials: one 256-thread workgroup per (row, Q head, 64-dim

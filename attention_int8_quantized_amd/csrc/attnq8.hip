@@ -83,43 +83,175 @@ int auto_rows_per_group(int G, int n_rows, int hd) {
 
 using KernelFn = void (*)(AttendArgs);
 
-template <int HD, bool QF32, bool FINAL>
+template <int HD, bool QF32, bool FINAL, int NQ, bool KV16>
+constexpr KernelFn kernel_of() {
+  if constexpr (KV16) return attend_f16kv_kernel<HD, QF32, FINAL, NQ>;
+  else return attend_q8_kernel<HD, QF32, FINAL, NQ>;
+}
+
+template <int HD, bool QF32, bool FINAL, bool KV16>
 KernelFn pick_nq(int nq) {
   switch (nq) {
-    case 2: if constexpr (HD >= 128) return attend_q8_kernel<HD, QF32, FINAL, 2>; else return nullptr;
-    case 3: if constexpr (HD == 256) return attend_q8_kernel<HD, QF32, FINAL, 3>; else return nullptr;
-    case 4: return attend_q8_kernel<HD, QF32, FINAL, 4>;
-    case 6: if constexpr (HD == 256) return attend_q8_kernel<HD, QF32, FINAL, 6>; else return nullptr;
-    case 8: return attend_q8_kernel<HD, QF32, FINAL, 8>;
+    case 2: if constexpr (HD >= 128) return kernel_of<HD, QF32, FINAL, 2, KV16>(); else return nullptr;
+    case 3: if constexpr (HD == 256) return kernel_of<HD, QF32, FINAL, 3, KV16>(); else return nullptr;
+    case 4: return kernel_of<HD, QF32, FINAL, 4, KV16>();
+    case 6: if constexpr (HD == 256) return kernel_of<HD, QF32, FINAL, 6, KV16>(); else return nullptr;
+    // an fp16 ring at head_dim 256 leaves no LDS for eight vector tiles
+    case 8: if constexpr (!(KV16 && HD == 256)) return kernel_of<HD, QF32, FINAL, 8, KV16>(); else return nullptr;
     default: return nullptr;
   }
 }
 
-template <bool FINAL>
+template <bool FINAL, bool KV16 = false>
 KernelFn pick_kernel(int hd, bool qf32, int nq) {
   switch (hd) {
-    case 64: return qf32 ? pick_nq<64, true, FINAL>(nq) : pick_nq<64, false, FINAL>(nq);
-    case 128: return qf32 ? pick_nq<128, true, FINAL>(nq) : pick_nq<128, false, FINAL>(nq);
-    case 256: return qf32 ? pick_nq<256, true, FINAL>(nq) : pick_nq<256, false, FINAL>(nq);
+    case 64: return qf32 ? pick_nq<64, true, FINAL, KV16>(nq) : pick_nq<64, false, FINAL, KV16>(nq);
+    case 128: return qf32 ? pick_nq<128, true, FINAL, KV16>(nq) : pick_nq<128, false, FINAL, KV16>(nq);
+    case 256: return qf32 ? pick_nq<256, true, FINAL, KV16>(nq) : pick_nq<256, false, FINAL, KV16>(nq);
     default: return nullptr;
   }
 }
 
-int check_kv(const void* q, int q_dtype, const int8_t* kc, const uint16_t* ks, const int8_t* vc,
+// Largest row group (query vectors) per workgroup: 128, except for an fp16
+// cache at head_dim 256 (its ring leaves LDS for six vector tiles).
+template <bool KV16>
+int max_vectors(int hd) { return KV16 && hd == 256 ? 96 : kMaxVectorsPerGroup; }
+
+// Checks shared by the attention calls (KV16: fp16 K/V, the scale pointers are unused).
+template <bool KV16>
+int check_kv(const void* q, int q_dtype, const void* kc, const uint16_t* ks, const void* vc,
              const uint16_t* vs, int hq, int hkv, int hd, int kv_stride) {
-  if (!q || !kc || !ks || !vc || !vs) return ATTNQ8_EINVAL;
+  if (!q || !kc || !vc) return ATTNQ8_EINVAL;
+  if (!KV16 && (!ks || !vs)) return ATTNQ8_EINVAL;
   if (q_dtype != ATTNQ8_F32 && q_dtype != ATTNQ8_F16) return ATTNQ8_EINVAL;
   if (hq <= 0 || hkv <= 0 || hq % hkv != 0) return ATTNQ8_EINVAL;
   if (!head_dim_ok(hd)) return ATTNQ8_EUNSUPPORTED;
   if (hq / hkv > kMaxVectorsPerGroup) return ATTNQ8_EUNSUPPORTED;
   if (kv_stride <= 0) return ATTNQ8_EINVAL;
   // per-head cache bytes are addressed with 32-bit buffer offsets
-  if ((long long)kv_stride * hd >= (1LL << 31) - 64) return ATTNQ8_EINVAL;
+  if ((long long)kv_stride * hd * (KV16 ? 2 : 1) >= (1LL << 31) - 64) return ATTNQ8_EINVAL;
   if (!aligned(q, 16) || !aligned(kc, 16) || !aligned(vc, 16)) return ATTNQ8_EALIGN;
-  if (!aligned(ks, 4) || !aligned(vs, 4)) return ATTNQ8_EALIGN;
+  if (!KV16 && (!aligned(ks, 4) || !aligned(vs, 4))) return ATTNQ8_EALIGN;
   return ATTNQ8_OK;
 }
 
+// Verify launch for either cache format (KV16: fp16 K/V in k, v; no scales).
+template <bool KV16>
+int verify_launch(const void* q, int q_dtype, const void* k, const uint16_t* k_scales, const void* v,
+                  const uint16_t* v_scales, int n_q_heads, int n_kv_heads, int head_dim,
+                  int kv_stride, int ctx_len, int n_rows, int rows_per_group, int n_splits,
+                  void* workspace, size_t workspace_bytes, float sm_scale, void* stream) {
+  int st = check_kv<KV16>(q, q_dtype, k, k_scales, v, v_scales, n_q_heads, n_kv_heads, head_dim,
+                          kv_stride);
+  if (st) return st;
+  if (ctx_len < 0 || n_rows < 1 || n_rows > 32) return ATTNQ8_EINVAL;
+  if ((long long)ctx_len + n_rows > kv_stride) return ATTNQ8_EINVAL;
+  if (rows_per_group < 0 || n_splits < 0) return ATTNQ8_EINVAL;
+  if (!(sm_scale >= 0.0f) || isinf(sm_scale)) return ATTNQ8_EINVAL;
+  const int G = n_q_heads / n_kv_heads;
+  if (rows_per_group * G > kMaxVectorsPerGroup) return ATTNQ8_EINVAL;
+  const int rg = rows_per_group > 0 ? rows_per_group : auto_rows_per_group(G, n_rows, head_dim);
+  if (rg * G > max_vectors<KV16>(head_dim)) return ATTNQ8_EUNSUPPORTED;
+  const int groups = (n_rows + rg - 1) / rg;
+  const int n_keys = ctx_len + n_rows;
+  const int tiles = (n_keys + 31) / 32;
+  const int S = n_splits > 0 ? n_splits : splits_for(n_keys, groups * n_kv_heads, head_dim);
+  if (S > tiles || S > 65535) return ATTNQ8_EINVAL;
+  if (!workspace) return ATTNQ8_EINVAL;
+  if (!aligned(workspace, 16)) return ATTNQ8_EALIGN;
+  const size_t need = attn_verify_q8_workspace_bytes(n_rows, n_q_heads, head_dim, S);
+  if (workspace_bytes < need) return ATTNQ8_EWORKSPACE;
+
+  st = device_status();
+  if (st) return st;
+
+  const int nq = nq_for(rg * G, head_dim);
+  KernelFn fn = pick_kernel<false, KV16>(head_dim, q_dtype == ATTNQ8_F32, nq);
+  if (!fn) return ATTNQ8_EUNSUPPORTED;
+  AttendArgs a;
+  a.q = q;
+  a.kc = (const int8_t*)k;
+  a.ks = k_scales;
+  a.vc = (const int8_t*)v;
+  a.vs = v_scales;
+  a.part_o = (float*)workspace;
+  a.part_ml = (float2*)((char*)workspace + (size_t)S * n_rows * n_q_heads * head_dim * sizeof(float));
+  a.out = nullptr;
+  a.Hq = n_q_heads;
+  a.G = G;
+  a.kv_stride = kv_stride;
+  a.pos0 = ctx_len;
+  a.n_rows = n_rows;
+  a.rows_per_wg = rg;
+  a.n_splits = S;
+  const float scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)head_dim));
+  a.kmul = (float)((double)scale * kLog2e);
+  hipLaunchKernelGGL(fn, dim3(S, groups, n_kv_heads), dim3(64 * kWaves), 0, (hipStream_t)stream, a);
+  st = launch_status();
+  if (st) return st;
+  snprintf(g_last_path, sizeof(g_last_path),
+           "verify kv%s hd%d q%s tiles%d rows_per_group%d groups%d splits%d kv_heads%d",
+           KV16 ? "f16" : "q8", head_dim, q_dtype == ATTNQ8_F32 ? "f32" : "f16", nq, rg, groups, S,
+           n_kv_heads);
+  return ATTNQ8_OK;
+}
+
+// Prompt launch for either cache format.
+template <bool KV16>
+int prompt_launch(const void* q, int q_dtype, const void* k, const uint16_t* k_scales, const void* v,
+                  const uint16_t* v_scales, int n_q_heads, int n_kv_heads, int head_dim,
+                  int kv_stride, int kv_len, int q_pos0, int n_queries, float sm_scale, float* out,
+                  void* stream) {
+  int st = check_kv<KV16>(q, q_dtype, k, k_scales, v, v_scales, n_q_heads, n_kv_heads, head_dim,
+                          kv_stride);
+  if (st) return st;
+  if (!out) return ATTNQ8_EINVAL;
+  if (!aligned(out, 16)) return ATTNQ8_EALIGN;
+  if (n_queries < 1 || q_pos0 < 0 || kv_len < 1) return ATTNQ8_EINVAL;
+  if ((long long)q_pos0 + n_queries > kv_len || kv_len > kv_stride) return ATTNQ8_EINVAL;
+  if (!(sm_scale >= 0.0f) || isinf(sm_scale)) return ATTNQ8_EINVAL;
+  const int G = n_q_heads / n_kv_heads;
+  if (G > max_vectors<KV16>(head_dim)) return ATTNQ8_EUNSUPPORTED;
+  // rows per workgroup: queries whose G heads fill up to 8 waves of 16 vectors,
+  // keeping about one workgroup per CU for the chunk
+  int rq = max_vectors<KV16>(head_dim) / G;
+  if (rq < 1) rq = 1;
+  const int per_cu = (n_queries * n_kv_heads + kTargetCUs - 1) / kTargetCUs;
+  if (rq > per_cu) rq = per_cu;
+  if (rq < 1) rq = 1;
+  const int groups = (n_queries + rq - 1) / rq;
+  if (groups > 65535) return ATTNQ8_EINVAL;
+  st = device_status();
+  if (st) return st;
+  const int nq = nq_for(rq * G, head_dim);
+  KernelFn fn = pick_kernel<true, KV16>(head_dim, q_dtype == ATTNQ8_F32, nq);
+  if (!fn) return ATTNQ8_EUNSUPPORTED;
+  AttendArgs a;
+  a.q = q;
+  a.kc = (const int8_t*)k;
+  a.ks = k_scales;
+  a.vc = (const int8_t*)v;
+  a.vs = v_scales;
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
+  a.out = out;
+  a.Hq = n_q_heads;
+  a.G = G;
+  a.kv_stride = kv_stride;
+  a.pos0 = q_pos0;
+  a.n_rows = n_queries;
+  a.rows_per_wg = rq;
+  a.n_splits = 1;
+  const float scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)head_dim));
+  a.kmul = (float)((double)scale * kLog2e);
+  hipLaunchKernelGGL(fn, dim3(1, groups, n_kv_heads), dim3(64 * kWaves), 0, (hipStream_t)stream, a);
+  st = launch_status();
+  if (st) return st;
+  snprintf(g_last_path, sizeof(g_last_path),
+           "prompt kv%s hd%d q%s tiles%d rows_per_group%d groups%d kv_heads%d", KV16 ? "f16" : "q8",
+           head_dim, q_dtype == ATTNQ8_F32 ? "f32" : "f16", nq, rq, groups, n_kv_heads);
+  return ATTNQ8_OK;
+}
 }  // namespace
 
 extern "C" {
@@ -161,57 +293,18 @@ int attn_verify_q8(const void* q, int q_dtype, const int8_t* k_codes, const uint
                    int head_dim, int kv_stride, int ctx_len, int n_rows, int rows_per_group,
                    int n_splits, void* workspace, size_t workspace_bytes, float sm_scale,
                    void* stream) {
-  int st = check_kv(q, q_dtype, k_codes, k_scales, v_codes, v_scales, n_q_heads, n_kv_heads,
-                    head_dim, kv_stride);
-  if (st) return st;
-  if (ctx_len < 0 || n_rows < 1 || n_rows > 32) return ATTNQ8_EINVAL;
-  if ((long long)ctx_len + n_rows > kv_stride) return ATTNQ8_EINVAL;
-  if (rows_per_group < 0 || n_splits < 0) return ATTNQ8_EINVAL;
-  if (!(sm_scale >= 0.0f) || isinf(sm_scale)) return ATTNQ8_EINVAL;
-  const int G = n_q_heads / n_kv_heads;
-  if (rows_per_group * G > kMaxVectorsPerGroup) return ATTNQ8_EINVAL;
-  const int rg = rows_per_group > 0 ? rows_per_group : auto_rows_per_group(G, n_rows, head_dim);
-  const int groups = (n_rows + rg - 1) / rg;
-  const int n_keys = ctx_len + n_rows;
-  const int tiles = (n_keys + 31) / 32;
-  const int S = n_splits > 0 ? n_splits : splits_for(n_keys, groups * n_kv_heads, head_dim);
-  if (S > tiles || S > 65535) return ATTNQ8_EINVAL;
-  if (!workspace) return ATTNQ8_EINVAL;
-  if (!aligned(workspace, 16)) return ATTNQ8_EALIGN;
-  const size_t need = attn_verify_q8_workspace_bytes(n_rows, n_q_heads, head_dim, S);
-  if (workspace_bytes < need) return ATTNQ8_EWORKSPACE;
+  return verify_launch<false>(q, q_dtype, k_codes, k_scales, v_codes, v_scales, n_q_heads,
+                              n_kv_heads, head_dim, kv_stride, ctx_len, n_rows, rows_per_group,
+                              n_splits, workspace, workspace_bytes, sm_scale, stream);
+}
 
-  st = device_status();
-  if (st) return st;
-
-  const int nq = nq_for(rg * G, head_dim);
-  KernelFn fn = pick_kernel<false>(head_dim, q_dtype == ATTNQ8_F32, nq);
-  if (!fn) return ATTNQ8_EUNSUPPORTED;
-  AttendArgs a;
-  a.q = q;
-  a.kc = k_codes;
-  a.ks = k_scales;
-  a.vc = v_codes;
-  a.vs = v_scales;
-  a.part_o = (float*)workspace;
-  a.part_ml = (float2*)((char*)workspace + (size_t)S * n_rows * n_q_heads * head_dim * sizeof(float));
-  a.out = nullptr;
-  a.Hq = n_q_heads;
-  a.G = G;
-  a.kv_stride = kv_stride;
-  a.pos0 = ctx_len;
-  a.n_rows = n_rows;
-  a.rows_per_wg = rg;
-  a.n_splits = S;
-  const float scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)head_dim));
-  a.kmul = (float)((double)scale * kLog2e);
-  hipLaunchKernelGGL(fn, dim3(S, groups, n_kv_heads), dim3(64 * kWaves), 0, (hipStream_t)stream, a);
-  st = launch_status();
-  if (st) return st;
-  snprintf(g_last_path, sizeof(g_last_path),
-           "verify hd%d q%s tiles%d rows_per_group%d groups%d splits%d kv_heads%d", head_dim,
-           q_dtype == ATTNQ8_F32 ? "f32" : "f16", nq, rg, groups, S, n_kv_heads);
-  return ATTNQ8_OK;
+int attn_verify_f16kv(const void* q, int q_dtype, const uint16_t* k, const uint16_t* v,
+                      int n_q_heads, int n_kv_heads, int head_dim, int kv_stride, int ctx_len,
+                      int n_rows, int rows_per_group, int n_splits, void* workspace,
+                      size_t workspace_bytes, float sm_scale, void* stream) {
+  return verify_launch<true>(q, q_dtype, k, nullptr, v, nullptr, n_q_heads, n_kv_heads, head_dim,
+                             kv_stride, ctx_len, n_rows, rows_per_group, n_splits, workspace,
+                             workspace_bytes, sm_scale, stream);
 }
 
 int attn_reduce_partials(const void* workspace, size_t workspace_bytes, int n_rows, int n_q_heads,
@@ -245,54 +338,16 @@ int attn_prompt_q8(const void* q, int q_dtype, const int8_t* k_codes, const uint
                    const int8_t* v_codes, const uint16_t* v_scales, int n_q_heads, int n_kv_heads,
                    int head_dim, int kv_stride, int kv_len, int q_pos0, int n_queries,
                    float sm_scale, float* out, void* stream) {
-  int st = check_kv(q, q_dtype, k_codes, k_scales, v_codes, v_scales, n_q_heads, n_kv_heads,
-                    head_dim, kv_stride);
-  if (st) return st;
-  if (!out) return ATTNQ8_EINVAL;
-  if (!aligned(out, 16)) return ATTNQ8_EALIGN;
-  if (n_queries < 1 || q_pos0 < 0 || kv_len < 1) return ATTNQ8_EINVAL;
-  if ((long long)q_pos0 + n_queries > kv_len || kv_len > kv_stride) return ATTNQ8_EINVAL;
-  if (!(sm_scale >= 0.0f) || isinf(sm_scale)) return ATTNQ8_EINVAL;
-  const int G = n_q_heads / n_kv_heads;
-  // rows per workgroup: queries whose G heads fill up to 8 waves of 16 vectors,
-  // keeping about one workgroup per CU for the chunk
-  int rq = kMaxVectorsPerGroup / G;
-  if (rq < 1) rq = 1;
-  const int per_cu = (n_queries * n_kv_heads + kTargetCUs - 1) / kTargetCUs;
-  if (rq > per_cu) rq = per_cu;
-  if (rq < 1) rq = 1;
-  const int groups = (n_queries + rq - 1) / rq;
-  if (groups > 65535) return ATTNQ8_EINVAL;
-  st = device_status();
-  if (st) return st;
-  const int nq = nq_for(rq * G, head_dim);
-  KernelFn fn = pick_kernel<true>(head_dim, q_dtype == ATTNQ8_F32, nq);
-  if (!fn) return ATTNQ8_EUNSUPPORTED;
-  AttendArgs a;
-  a.q = q;
-  a.kc = k_codes;
-  a.ks = k_scales;
-  a.vc = v_codes;
-  a.vs = v_scales;
-  a.part_o = nullptr;
-  a.part_ml = nullptr;
-  a.out = out;
-  a.Hq = n_q_heads;
-  a.G = G;
-  a.kv_stride = kv_stride;
-  a.pos0 = q_pos0;
-  a.n_rows = n_queries;
-  a.rows_per_wg = rq;
-  a.n_splits = 1;
-  const float scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)head_dim));
-  a.kmul = (float)((double)scale * kLog2e);
-  hipLaunchKernelGGL(fn, dim3(1, groups, n_kv_heads), dim3(64 * kWaves), 0, (hipStream_t)stream, a);
-  st = launch_status();
-  if (st) return st;
-  snprintf(g_last_path, sizeof(g_last_path),
-           "prompt hd%d q%s tiles%d rows_per_group%d groups%d kv_heads%d", head_dim,
-           q_dtype == ATTNQ8_F32 ? "f32" : "f16", nq, rq, groups, n_kv_heads);
-  return ATTNQ8_OK;
+  return prompt_launch<false>(q, q_dtype, k_codes, k_scales, v_codes, v_scales, n_q_heads,
+                              n_kv_heads, head_dim, kv_stride, kv_len, q_pos0, n_queries, sm_scale,
+                              out, stream);
+}
+
+int attn_prompt_f16kv(const void* q, int q_dtype, const uint16_t* k, const uint16_t* v,
+                      int n_q_heads, int n_kv_heads, int head_dim, int kv_stride, int kv_len,
+                      int q_pos0, int n_queries, float sm_scale, float* out, void* stream) {
+  return prompt_launch<true>(q, q_dtype, k, nullptr, v, nullptr, n_q_heads, n_kv_heads, head_dim,
+                             kv_stride, kv_len, q_pos0, n_queries, sm_scale, out, stream);
 }
 
 int attn_kv_append_q8(const void* k, const void* v, int x_dtype, int n_tokens, int n_kv_heads,

@@ -13,6 +13,7 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef int v2i32_t __attribute__((ext_vector_type(2)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
 
 // A raw (unswizzled, stride 0) buffer resource over [base, base + bytes):
 // loads at offsets >= bytes return zero and access no memory.  The third

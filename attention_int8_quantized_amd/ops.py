@@ -122,6 +122,70 @@ def prompt(q, k_codes, k_scales, v_codes, v_scales, q_pos0: int, kv_len: Optiona
     return out
 
 
+def _check_cache16(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if q.dtype not in _QTYPES:
+        raise ValueError("q must be float32 or float16")
+    if k.dtype != torch.float16 or v.dtype != torch.float16:
+        raise ValueError("an fp16 cache holds float16 K and V")
+    if q.dim() != 3 or k.dim() != 3 or k.shape != v.shape:
+        raise ValueError("q [rows][Hq][hd], k and v [Hkv][stride][hd]")
+    hkv, stride, hd = k.shape
+    if q.shape[2] != hd:
+        raise ValueError("inconsistent head_dim")
+    return q.shape[0], q.shape[1], hkv, hd, stride
+
+
+def verify_f16kv(q, k, v, ctx_len: int, rows_per_group: int = 0, n_splits: int = 0,
+                 sm_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Verify attention over an fp16 cache: attn_verify_f16kv then attn_reduce_partials."""
+    n_rows, hq, hkv, hd, stride = _check_cache16(q, k, v)
+    lib = _lib.load()
+    S = n_splits or verify_splits(hq, hkv, hd, ctx_len, n_rows, rows_per_group)
+    need = workspace_bytes(n_rows, hq, hd, S)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = lib.attn_verify_f16kv(_ptr(q), _QTYPES[q.dtype], _ptr(k), _ptr(v), hq, hkv, hd, stride,
+                               ctx_len, n_rows, rows_per_group, S, _ptr(workspace),
+                               workspace.numel(), float(sm_scale), _stream())
+    _lib.check("attn_verify_f16kv", st)
+    return reduce_partials(workspace, n_rows, hq, hd, S, out)
+
+
+def verify_f16kv_partials(q, k, v, ctx_len: int, rows_per_group: int = 0, n_splits: int = 0,
+                          sm_scale: float = 0.0,
+                          workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, int]:
+    """attn_verify_f16kv alone; returns (workspace, n_splits)."""
+    n_rows, hq, hkv, hd, stride = _check_cache16(q, k, v)
+    S = n_splits or verify_splits(hq, hkv, hd, ctx_len, n_rows, rows_per_group)
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes(n_rows, hq, hd, S), dtype=torch.uint8,
+                                device=q.device)
+    st = _lib.load().attn_verify_f16kv(_ptr(q), _QTYPES[q.dtype], _ptr(k), _ptr(v), hq, hkv, hd,
+                                       stride, ctx_len, n_rows, rows_per_group, S, _ptr(workspace),
+                                       workspace.numel(), float(sm_scale), _stream())
+    _lib.check("attn_verify_f16kv", st)
+    return workspace, S
+
+
+def prompt_f16kv(q, k, v, q_pos0: int, kv_len: Optional[int] = None, sm_scale: float = 0.0,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Causal prompt attention over an fp16 cache."""
+    n, hq, hkv, hd, stride = _check_cache16(q, k, v)
+    if kv_len is None:
+        kv_len = q_pos0 + n
+    if out is None:
+        out = torch.empty((n, hq, hd), dtype=torch.float32, device=q.device)
+    st = _lib.load().attn_prompt_f16kv(_ptr(q), _QTYPES[q.dtype], _ptr(k), _ptr(v), hq, hkv, hd,
+                                       stride, kv_len, q_pos0, n, float(sm_scale), _ptr(out),
+                                       _stream())
+    _lib.check("attn_prompt_f16kv", st)
+    return out
+
+
 def kv_append(k: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, pos0: int,
               v: Optional[torch.Tensor] = None, v_codes: Optional[torch.Tensor] = None,
               v_scales: Optional[torch.Tensor] = None) -> None:

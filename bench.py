@@ -276,6 +276,7 @@ def main():
     if not args.no_append:
         res["kv_append"] = time_append(ops, dev, min(K, 20), args.warmup)
         res["verify_head"] = time_head(ops, dev, min(K, 20), args.warmup)
+        res.update(time_f16kv(ops, dev, wv, wp, min(K, 20), args.warmup, not args.no_prompt))
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wv, iv)
@@ -364,6 +365,84 @@ def time_append(ops, dev, steps, warmup):
         "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
         "steps": steps,
     }
+
+
+def _events_mean(call, steps, warmup):
+    import torch
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ev = [(E(), E()) for _ in range(steps)]
+    torch.cuda._sleep(int(2.4e9 * (0.05e-3 * steps + 0.02)))
+    for i in range(steps):
+        ev[i][0].record()
+        call(i + 1)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+
+
+def time_f16kv(ops, dev, wv, wp, steps, warmup, with_prompt):
+    """The verify and prompt workloads over an fp16 K/V cache (the same seeded
+    draws rounded to fp16 instead of quantised), measured beside the int8 path."""
+    import torch
+
+    import workloads as W
+
+    out = {}
+    iv = W.generate_f16kv(wv)
+    base = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (iv.q, iv.k, iv.v)]
+    kvb = base[1].numel() * 2 + base[2].numel() * 2
+    copies = [base] + [[t.clone() for t in base] for _ in range(max(0, int(1.1e9 // kvb)))]
+    S = ops.verify_splits(wv.n_q_heads, wv.n_kv_heads, wv.head_dim, wv.ctx_len, wv.n_rows, 0)
+    ws = torch.empty(ops.workspace_bytes(wv.n_rows, wv.n_q_heads, wv.head_dim, S),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty((wv.n_rows, wv.n_q_heads, wv.head_dim), dtype=torch.float32, device=dev)
+
+    def vcall(i):
+        q, k, v = copies[i % len(copies)]
+        ops.verify_f16kv_partials(q, k, v, ctx_len=wv.ctx_len, n_splits=S, workspace=ws)
+
+    vcall(0)
+    vpath = ops.last_path()
+    t = _events_mean(vcall, steps, warmup)
+    vis = wv.visible_kv_bytes() // (2 * (wv.head_dim + wv.head_dim // 16)) * 4 * wv.head_dim
+    out["verify_f16kv"] = {
+        "workload": f"{wv.name} over an fp16 cache",
+        "path": vpath,
+        "kernel_us": round(t * 1e6, 3),
+        "kv_bytes": vis,
+        "gbs": round(vis / t / 1e9, 1),
+        "frac_hbm": round(vis / t / 1e9 / HBM_PEAK_GBS, 4),
+        "rotating_copies": len(copies),
+    }
+    ops.reduce_partials(ws, wv.n_rows, wv.n_q_heads, wv.head_dim, S, out=o)
+    del copies, base
+    if with_prompt:
+        ip = W.generate_f16kv(wp)
+        pb = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (ip.q, ip.k, ip.v)]
+        pout = torch.empty((wp.n_queries, wp.n_q_heads, wp.head_dim), dtype=torch.float32,
+                           device=dev)
+        pcopies = [pb] + [[t.clone() for t in pb] for _ in range(7)]
+
+        def pcall(i):
+            q, k, v = pcopies[i % len(pcopies)]
+            ops.prompt_f16kv(q, k, v, q_pos0=wp.pos0, kv_len=wp.kv_len, out=pout)
+
+        pcall(0)
+        ppath = ops.last_path()
+        tp = _events_mean(pcall, max(3, steps // 4), 1)
+        tf = wp.algorithmic_flops() / tp / 1e12
+        out["prompt_f16kv"] = {
+            "workload": f"{wp.name} over an fp16 cache",
+            "path": ppath,
+            "ms_per_call": round(tp * 1e3, 4),
+            "tflops": round(tf, 2),
+            "frac_mfma": round(tf / FP16_MFMA_PEAK_TFLOPS, 4),
+        }
+    return out
 
 
 # The verify head measured beside the attention: greedy token and top

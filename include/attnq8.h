@@ -130,6 +130,33 @@ int attn_prompt_q8(const void* q, int q_dtype,
                    float sm_scale, float* out, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * The same two attention shapes over an fp16 K/V cache ("hip: gfx12 (RDNA4)
+ * WMMA kernel for the int8-KV QSA prompt attention", What: fp16 KV pools stay
+ * with the earlier kernel; the operation is the one above with Khat = K and
+ * Vhat = V, no scales).
+ *
+ * k, v: fp16 bit patterns [n_kv_heads][kv_stride][head_dim], 16-byte aligned.
+ * Every other argument, the workspace layout, the reducer and the errors are
+ * those of attn_verify_q8 / attn_prompt_q8, with one limit more: at head_dim
+ * 256 a row group holds at most 96 query vectors (rows_per_group * n_q_heads /
+ * n_kv_heads <= 96; the automatic grouping stays within it), else
+ * ATTNQ8_EUNSUPPORTED.  Sizes and splits come from attn_verify_q8_splits and
+ * attn_verify_q8_workspace_bytes.
+ * ------------------------------------------------------------------------- */
+int attn_verify_f16kv(const void* q, int q_dtype,
+                      const uint16_t* k, const uint16_t* v,
+                      int n_q_heads, int n_kv_heads, int head_dim,
+                      int kv_stride, int ctx_len, int n_rows,
+                      int rows_per_group, int n_splits,
+                      void* workspace, size_t workspace_bytes,
+                      float sm_scale, void* stream);
+int attn_prompt_f16kv(const void* q, int q_dtype,
+                      const uint16_t* k, const uint16_t* v,
+                      int n_q_heads, int n_kv_heads, int head_dim,
+                      int kv_stride, int kv_len, int q_pos0, int n_queries,
+                      float sm_scale, float* out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * KV append: quantise n_tokens new K (and V) rows into the cache at positions
  * pos0 .. pos0 + n_tokens - 1 of every KV head.  The format is the pages' Q8
  * KV block ("perf(gfx1100): share Q8 KV scans across verifier rows", Summary;

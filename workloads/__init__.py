@@ -251,6 +251,46 @@ def generate(w) -> Inputs:
     return Inputs(w, q, kc, ks, vc, vs, peaked)
 
 
+@dataclass
+class Inputs16:
+    """A workload's inputs for an fp16 K/V cache (no scales)."""
+
+    workload: object
+    q: np.ndarray  # as for Inputs
+    k: np.ndarray  # float16 [Hkv][stride][hd]
+    v: np.ndarray
+
+
+def generate_f16kv(w) -> Inputs16:
+    """The same seeded draws as generate(), with K and V rounded to fp16 instead of
+    quantised to int8 blocks (the peaked-token multiplier applies as there)."""
+    rq, rk, rv, rp = _streams(w.seed)
+    hd, hkv, hq = w.head_dim, w.n_kv_heads, w.n_q_heads
+    T = w.kv_tokens
+    S = w.stride
+    if S < T:
+        raise ValueError("kv_stride smaller than the tokens in use")
+    if w.kind == "verify":
+        q = rq.standard_normal((w.n_rows, hq, hd), dtype=np.float32)
+    else:
+        q = rq.standard_normal((w.n_queries, hq, hd), dtype=np.float32).astype(np.float16)
+    k = rk.standard_normal((hkv, T, hd), dtype=np.float32)
+    v = rv.standard_normal((hkv, T, hd), dtype=np.float32)
+    frac = getattr(w, "peaked_frac", 0.0)
+    if frac > 0:
+        n = int(round(frac * T))
+        peaked = np.sort(rp.choice(T, size=n, replace=False))
+        k[:, peaked, :] *= np.float32(w.peaked_mult)
+    k16 = k.astype(np.float16)
+    v16 = v.astype(np.float16)
+    del k, v
+    if S > T:
+        pad = ((0, 0), (0, S - T), (0, 0))
+        k16 = np.pad(k16, pad)
+        v16 = np.pad(v16, pad)
+    return Inputs16(w, q, k16, v16)
+
+
 def describe(w) -> Dict[str, object]:
     d = {k: getattr(w, k) for k in w.__dataclass_fields__ if k != "kind"}
     d["kind"] = w.kind
