@@ -413,42 +413,25 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
   const int nq = (M + 15) >> 4;         // vector tiles (<= NQ, checked on the host)
   const int n_keys = a.pos0 + r0 + nr;  // keys 0 .. n_keys-1 are seen by some row
   const int n_tiles = (n_keys + 31) >> 5;
-  const int t_begin = (int)(((long long)split * n_tiles) / a.n_splits);
-  const int t_end = (int)(((long long)(split + 1) * n_tiles) / a.n_splits);
+  // this split's tiles [t_begin, t_end): 32-bit arithmetic while the products
+  // fit (the usual case), 64-bit otherwise
+  int t_begin, t_end;
+  if (n_tiles <= 32767 && a.n_splits <= 65535) {
+    t_begin = (int)((uint32_t)(split * n_tiles) / (uint32_t)a.n_splits);
+    t_end = (int)((uint32_t)((split + 1) * n_tiles) / (uint32_t)a.n_splits);
+  } else {
+    t_begin = (int)(((long long)split * n_tiles) / a.n_splits);
+    t_end = (int)(((long long)(split + 1) * n_tiles) / a.n_splits);
+  }
   const int k_end = min(n_keys, t_end * 32);
 
   // ---- QK role: vector tile `wave` (column n16 of its S^T tile)
-  const bool qk = wave < nq;  // wave-uniform
   const int v = wave * 16 + n16;
-  const bool v_ok = qk && v < M;
+  const bool v_ok = wave < nq && v < M;
   const int vr = v_ok ? v / a.G : 0;
   const int vh = v_ok ? g * a.G + (v - vr * a.G) : 0;
 
-  // ---- the q loads go out before the tile copies: the copies occupy this
-  // CU's share of HBM bandwidth for thousands of cycles, and q (an L2 hit for
-  // all but the first workgroup of a head) would otherwise return behind them
-  constexpr int QRAW = QF32 ? 2 * NB : NB;
-  float4_t qraw[QRAW];
-  const size_t qoff = ((size_t)(r0 + vr) * a.Hq + vh) * HD + 8 * h4;
-#pragma unroll
-  for (int k = 0; k < QRAW; ++k) qraw[k] = (float4_t){0, 0, 0, 0};
-  if (v_ok) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (QF32) {
-        const float4_t* p = (const float4_t*)((const float*)a.q + qoff + 32 * b);
-        qraw[2 * b] = p[0];
-        qraw[2 * b + 1] = p[1];
-      } else {
-        qraw[b] = *(const float4_t*)((const half_t*)a.q + qoff + 32 * b);
-      }
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- then the copies; tile t is copied D-2 iterations ahead into ring
+  // ---- the tile copier: tile t is copied D-2 iterations ahead into ring
   // stage t % D
   const size_t head_rows = (size_t)g * a.kv_stride;
   constexpr int NWI = R::NWI;
@@ -462,24 +445,21 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
   }
   cp.init(copies ? R::copy_index(wave) : NWI, lane);
   const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
-  if (copies) {
+  auto issue_first = [&](int n0, int n1) {
+    if (copies) {
 #pragma unroll
-    for (int s = 0; s < LEAD; ++s)
-      cp.issue(ring0 + s * L::BYTES, (t_begin + s) * 32, t_begin + s < t_end);
-  }
+      for (int s = n0; s < n1; ++s)
+        cp.issue(ring0 + s * L::BYTES, (t_begin + s) * 32, t_begin + s < t_end);
+    }
+  };
 
-  const int lim = v_ok ? a.pos0 + r0 + vr : -1;  // last key this vector sees
-  const int lim_eff = min(lim, k_end - 1);        // ... within this split
-  // the smallest of those over the wave's vectors (wave-uniform): tiles that end
-  // at or before it need no mask
-  int lim_min = v_ok ? lim_eff : 0x7fffffff;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) lim_min = min(lim_min, __shfl_xor(lim_min, o, 64));
-  lim_min = __builtin_amdgcn_readfirstlane(lim_min);
-
-  // The q fragments of the QK role, held across tiles (B operand of
-  // S^T = K Q^T; lane: vector n16, dims 32b + 8*h4 + e; hi in QR(b), lo in
-  // QR(NB + b)).  Each role loop below keeps its own accumulators.
+  // ---- the q loads and tile 0 go out first, the other tiles in flight only
+  // after a barrier: at the start every CU requests its tiles at once, and q
+  // (an L2 hit for all but the first workgroup of a head) and each CU's first
+  // tile would otherwise return behind the others' later tiles.  Loads and their use stay in one block, so the
+  // compiler's wait counting carries no q load into the other waves' loops
+  // (a wait placed there for a q register would also wait for every copy).
+  const bool qk = wave < nq;  // wave-uniform
   constexpr int NREG = QF32 && !QLO_LDS ? 2 * NB : NB;
   float4_t regs[NREG];
 #define QR(k) (__builtin_bit_cast(half8_t, regs[(k)]))
@@ -487,6 +467,27 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
   for (int k = 0; k < NREG; ++k) regs[k] = (float4_t){0, 0, 0, 0};
   float xmul = 0.0f;
   if (qk) {
+    constexpr int QRAW = QF32 ? 2 * NB : NB;
+    float4_t qraw[QRAW];
+    const size_t qoff = ((size_t)(r0 + vr) * a.Hq + vh) * HD + 8 * h4;
+#pragma unroll
+    for (int k = 0; k < QRAW; ++k) qraw[k] = (float4_t){0, 0, 0, 0};
+    if (v_ok) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        if (QF32) {
+          const float4_t* p = (const float4_t*)((const float*)a.q + qoff + 32 * b);
+          qraw[2 * b] = p[0];
+          qraw[2 * b + 1] = p[1];
+        } else {
+          qraw[b] = *(const float4_t*)((const half_t*)a.q + qoff + 32 * b);
+        }
+      }
+    }
+    issue_first(0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
     float qv[NB][8];
     float amax = 0.0f;
 #pragma unroll
@@ -529,7 +530,25 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
       if (QLO_LDS) *(half8_t*)(qlo_s + ((wave * NB + b) * 64 + lane) * 16) = lo8;
       else if (QF32) regs[NB + b] = __builtin_bit_cast(float4_t, lo8);
     }
+  } else {
+    issue_first(0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   }
+  issue_first(1, LEAD);
+
+  const int lim = v_ok ? a.pos0 + r0 + vr : -1;  // last key this vector sees
+  const int lim_eff = min(lim, k_end - 1);        // ... within this split
+  // the smallest of those over the wave's vectors (wave-uniform): tiles that end
+  // at or before it need no mask.  A vector's row grows with its index, so it
+  // is the wave's first vector's (valid for every QK wave).
+  const int lim_min = min(a.pos0 + r0 + (wave * 16) / a.G, k_end - 1);
+
+  // The q fragments of the QK role (set up above) are held across tiles as
+  // the B operand of S^T = K Q^T (lane: vector n16, dims 32b + 8*h4 + e; hi
+  // in QR(b), lo in QR(NB + b)).  Each role loop below keeps its own
+  // accumulators.
   float m_ref = -INFINITY;  // QK role: reference point of the vector (base 2)
   float l_part = 0.0f;      // QK role: this lane's share of the vector's sum
 
