@@ -642,20 +642,21 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
     // mask and online softmax (base 2), p -> fp16 hi + lo
     // (lanes past the last vector of the wave hold q = 0, hence finite values
     // that only reach their own, never written, outputs)
+    // (the maximum is taken on the unscaled dots: xmul > 0)
     float x[2][4];
     float tmax = -INFINITY;
     if (key0 + 31 <= lim_min) {
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[u][e] = s[u][e] * xmul;
+        for (int e = 0; e < 4; ++e) x[u][e] = s[u][e];
     } else {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int key = key0 + 16 * u + 4 * h4 + e;
-          x[u][e] = key <= lim_eff ? s[u][e] * xmul : -INFINITY;
+          x[u][e] = key <= lim_eff ? s[u][e] : -INFINITY;
         }
       }
     }
@@ -663,7 +664,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, x[u][e]);
-    tmax = wave_max_groups(tmax);
+    tmax = wave_max_groups(tmax) * xmul;
     const bool need = tmax > m_ref + kRescaleSlack;
     float alpha = 1.0f;
     if (__any(need)) {
@@ -680,14 +681,15 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        p[4 * u + e] = __builtin_amdgcn_exp2f(x[u][e] - mu);
+        p[4 * u + e] = __builtin_amdgcn_exp2f(fmaf(x[u][e], xmul, -mu));
         l_part += p[4 * u + e];
       }
     half8_t phi, plo;
 #pragma unroll
     for (int i = 0; i < 8; i += 2) {
       const half2_t h = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(p[i], p[i + 1]));
-      const half2_t l = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(p[i] - (float)h[0], p[i + 1] - (float)h[1]));
+      const half2_t l = __builtin_bit_cast(
+          half2_t, __builtin_amdgcn_cvt_pkrtz(fmaf(-(float)h[0], 1.0f, p[i]), fmaf(-(float)h[1], 1.0f, p[i + 1])));
       phi[i] = h[0];
       phi[i + 1] = h[1];
       plo[i] = l[0];
