@@ -364,6 +364,7 @@ def time_append(ops, dev, steps, warmup):
         "gbs": round(gbs, 1),
         "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
         "steps": steps,
+        "traffic": load_traffic("append"),
     }
 
 
@@ -417,6 +418,7 @@ def time_f16kv(ops, dev, wv, wp, steps, warmup, with_prompt):
         "gbs": round(vis / t / 1e9, 1),
         "frac_hbm": round(vis / t / 1e9 / HBM_PEAK_GBS, 4),
         "rotating_copies": len(copies),
+        "traffic": load_traffic("verify_f16kv"),
     }
     ops.reduce_partials(ws, wv.n_rows, wv.n_q_heads, wv.head_dim, S, out=o)
     del copies, base
@@ -441,6 +443,7 @@ def time_f16kv(ops, dev, wv, wp, steps, warmup, with_prompt):
             "ms_per_call": round(tp * 1e3, 4),
             "tflops": round(tf, 2),
             "frac_mfma": round(tf / FP16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": load_traffic("prompt_f16kv"),
         }
     return out
 
@@ -488,6 +491,7 @@ def time_head(ops, dev, steps, warmup):
         "gbs": round(moved / t / 1e9, 1),
         "frac_hbm": round(moved / t / 1e9 / HBM_PEAK_GBS, 4),
         "steps": steps,
+        "traffic": load_traffic("head"),
     }
 
 
