@@ -203,18 +203,24 @@ struct TileCopier {
 
   // Copy the tile starting at key0 into the stage at lds (zeros when !live:
   // the key offset then lies past every buffer range).
-  __device__ __forceinline__ void issue(uint32_t lds, int key0, bool live) const {
+  __device__ __forceinline__ void issue(uint32_t lds, int key0, bool live) const { issue_part(lds, key0, live, 0, 1); }
+
+  // Part `part` of `nparts` of those copies (code chunks split evenly, the
+  // scale copy with the last part), so that a wave can spread its copies
+  // between other work instead of queueing them back to back.
+  __device__ __forceinline__ void issue_part(uint32_t lds, int key0, bool live, int part, int nparts) const {
     const int k0 = live ? key0 : (1 << 22);  // wave-uniform
     if (codes) {
 #pragma unroll
       for (int r = 0; r < CPW; ++r) {
+        if (r * nparts < part * CPW || r * nparts >= (part + 1) * CPW) continue;
         const int off = k0 * L::ROW + code_off[r];
         dma_b128(kc, lds + L::K_OFF + code_lds[r], off);
         dma_b128(vc, lds + L::V_OFF + code_lds[r], off);
       }
     }
     if constexpr (L::SCALE_OPS > 0) {
-      if (s_op >= 0 && s_off >= 0) {
+      if (part == nparts - 1 && s_op >= 0 && s_off >= 0) {
         const int off = k0 * 2 * L::NB + s_off;
         if (s_op < L::SCALE_OPS) dma_b32(ks, lds + s_lds, off);
         else dma_b32(vs, lds + s_lds, off);
@@ -809,7 +815,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
         // this wave's copies of tile t+1 (int8: K converted now) or t landed
         if (KV16 ? has_qk : t + 1 < t_end) cp.template wait_all_but<WAIT_NEWER>();
         __syncthreads();  // K(t) converted; P(t-1) written; tile t+1 landed
-        if (has_qk) cp.issue(ring0 + ((slot + LEAD) % D) * L::BYTES, (t + LEAD) * 32, t + LEAD < t_end);
+        const uint32_t cdst = ring0 + ((slot + LEAD) % D) * L::BYTES;
         const uint8_t* st = ring + slot * L::BYTES;
         const uint8_t* stn = ring + ((slot + 1) % D) * L::BYTES;
         uint8_t* kfn = kfrag[(t + 1) & 1];
@@ -823,9 +829,11 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
             }
           }
         };
+        // the copies of tile t+LEAD go out one share before each block's V
         half8_t vnh[BPW][2], vnl[BPW][2];
 #pragma unroll
         for (int jb = 0; jb < BPW; ++jb) {
+          if (has_qk) cp.issue_part(cdst, (t + LEAD) * 32, t + LEAD < t_end, jb, BPW);
           if constexpr (KV16) read_v16<HD>(R::block(wave, jb), st, lane, vnh[jb]);
           else convert_v<HD>(R::block(wave, jb), st, lane, vnh[jb], vnl[jb]);
         }
