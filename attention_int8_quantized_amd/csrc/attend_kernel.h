@@ -1029,7 +1029,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_partials_kernel(const f
   constexpr int LPS = kReduceDims / 4;          // lanes per split slot
   constexpr int NSLOT = kReduceThreads / LPS;   // split slots
   constexpr int NWAVE = kReduceThreads / 64;
-  constexpr int B = 8;                          // splits in flight per lane
+  constexpr int B = 4;                          // splits in flight per lane
   __shared__ float wmax[NWAVE];
   __shared__ float4_t slot_acc[NSLOT][LPS];
   __shared__ float slot_den[NSLOT];
