@@ -68,6 +68,8 @@ SMALL = [
     (64, 1, 128, 70, 2, 0, 0, np.float32, 0),   # 128 query vectors in one group
     (128, 1, 64, 45, 1, 0, 0, np.float32, 1),   # 8 waves, one row
     (24, 4, 256, 2000, 8, 0, 63, np.float32, 0),  # every split 1 tile
+    (24, 4, 256, 777, 32, 0, 0, np.float32, 5),   # 32 rows: groups of 10, 10, 10, 2
+    (24, 4, 256, 777, 32, 0, 0, np.float16, 0),
 ]
 
 
@@ -206,3 +208,45 @@ def test_bad_arguments_on_gpu():
         ops.verify_partials(q, kc, ks, vc, vs, ctx_len=w.ctx_len, workspace=small)
     with pytest.raises(Exception):
         ops.verify(q, kc, ks, vc, vs, ctx_len=w.ctx_len + 1)  # rows run past the cache
+
+
+def test_dominant_logit_selects_its_value():
+    """One key's logit exceeds the others by 31.75: the output is that key's Vhat
+    (the other keys weigh at most 49 e^-31.75 ~ 8e-13 in all, far below the
+    kernel's hi+lo rounding, bounded here by 2^-20 of max|Vhat|)."""
+    hd, T = 64, 50
+    w = W.VerifyWorkload("dominant", 1, 1, hd, T - 1, 1, 1, seed=14)
+    inp = W.generate(w)
+    rng = np.random.default_rng(14)
+    inp.k_codes[:] = 0
+    inp.k_scales[:] = np.float16(0.01)
+    tstar = 23
+    inp.k_codes[0, tstar, 0] = 127
+    inp.k_scales[0, tstar, 0] = np.float16(2.0)
+    inp.v_codes[:] = rng.integers(-127, 128, size=inp.v_codes.shape).astype(np.int8)
+    inp.v_scales[:] = np.float16(0.02)
+    inp.q[:] = 0
+    inp.q[0, 0, 0] = 1.0
+    _, got, _ = run_verify(w, inp=inp)
+    vhat = oracle.dequantize(inp.v_codes, inp.v_scales)
+    assert np.max(np.abs(got[0, 0] - vhat[0, tstar])) <= 2.0 ** -20 * np.abs(vhat).max()
+
+
+def test_verify_window_inside_convex_hull():
+    """Every output element lies between the smallest and largest Vhat of its
+    visible keys (up to fp32 rounding of the weighted mean)."""
+    w = W.VERIFY_WINDOW
+    note("verify window: convex hull of the visible values")
+    inp, got, _ = run_verify(w)
+    G = w.n_q_heads // w.n_kv_heads
+    for g in range(w.n_kv_heads):
+        vhat = oracle.dequantize(inp.v_codes[g, : w.ctx_len + w.n_rows], inp.v_scales[g, : w.ctx_len + w.n_rows])
+        tol = 1e-6 * np.abs(vhat).max()
+        lo = vhat[: w.ctx_len + 1].min(axis=0)
+        hi = vhat[: w.ctx_len + 1].max(axis=0)
+        for r in range(w.n_rows):
+            if r > 0:
+                lo = np.minimum(lo, vhat[w.ctx_len + r])
+                hi = np.maximum(hi, vhat[w.ctx_len + r])
+            out = got[r, g * G:(g + 1) * G]
+            assert np.all(out >= lo - tol) and np.all(out <= hi + tol), f"row {r} KV head {g}"
