@@ -62,6 +62,7 @@ _SIGNATURES = {
     "attn_verify_head_greedy": (
         _c_int, [_vp, _c_int, _c_int, ctypes.c_longlong, _vp, _vp, _vp, _c_size, _vp]),
     "attnq8_selftest_i8_to_f16": (_c_int, [_vp, _vp]),
+    "attnq8_stream_read": (_c_int, [_vp, _c_size, _vp, _vp]),
     "attnq8_status_string": (ctypes.c_char_p, [_c_int]),
     "attnq8_last_path": (ctypes.c_char_p, []),
 }

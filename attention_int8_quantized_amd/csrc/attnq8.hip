@@ -11,6 +11,7 @@
 #include "append_kernel.h"
 #include "attend_kernel.h"
 #include "head_kernel.h"
+#include "stream_kernel.h"
 
 namespace {
 
@@ -459,6 +460,20 @@ int attnq8_selftest_i8_to_f16(uint16_t* out, void* stream) {
   if (st) return st;
   hipLaunchKernelGGL(selftest_i8_to_f16_kernel, dim3(256), dim3(256), 0, (hipStream_t)stream, out);
   return launch_status();
+}
+
+int attnq8_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  static_assert(ATTNQ8_STREAM_SINK_WORDS == kStreamBlocks, "one sink word per workgroup");
+  if (!sink || (!buf && bytes > 0)) return ATTNQ8_EINVAL;
+  if (!aligned(buf, 16) || bytes % 16 != 0 || !aligned(sink, 4)) return ATTNQ8_EALIGN;
+  int st = device_status();
+  if (st) return st;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(kStreamBlocks), dim3(kStreamThreads), 0, (hipStream_t)stream,
+                     (const uint4*)buf, bytes / 16, sink);
+  st = launch_status();
+  if (st) return st;
+  snprintf(g_last_path, sizeof(g_last_path), "stream_read bytes%zu", bytes);
+  return ATTNQ8_OK;
 }
 
 }  // extern "C"

@@ -255,5 +255,24 @@ def selftest_i8_to_f16(device="cuda") -> torch.Tensor:
     return out
 
 
+STREAM_SINK_WORDS = 1024
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Tensor:
+    """Read every byte of a contiguous device tensor (its size a multiple of 16
+    bytes) with the library's plain read kernel; returns the 1,024-word sink
+    whose XOR is the XOR of the buffer's 32-bit words."""
+    if not buf.is_contiguous():
+        raise ValueError("stream_read needs a contiguous tensor")
+    if sink is None:
+        sink = torch.empty(STREAM_SINK_WORDS, dtype=torch.int32, device=buf.device)
+    if sink.numel() * sink.element_size() < 4 * STREAM_SINK_WORDS:
+        raise ValueError("stream_read needs a sink of 1,024 32-bit words")
+    _lib.check("attnq8_stream_read",
+               _lib.load().attnq8_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                                              _stream()))
+    return sink
+
+
 def last_path() -> str:
     return _lib.last_path()

@@ -280,6 +280,10 @@ def main():
             "traffic": load_traffic("prompt"),
         }
     res["host_wall_s"] = round(wall, 3)
+    ceil = read_ceiling(ops, dev)
+    res["read_ceiling"] = ceil
+    res["verify"]["frac_of_read_ceiling"] = round(gbs / ceil["gbs"], 4)
+    res["verify"]["kernel_frac_of_read_ceiling"] = round(k1_gbs / ceil["gbs"], 4)
     if not args.no_append:
         res["kv_append"] = time_append(ops, dev, min(K, 20), args.warmup)
         res["verify_head"] = time_head(ops, dev, min(K, 20), args.warmup)
@@ -289,6 +293,30 @@ def main():
         res["cpu_baseline"] = cpu_baseline(wv, iv)
 
     print(json.dumps(res), flush=True)
+
+
+def read_ceiling(ops, dev, nbytes=1 << 30, reps=10):
+    """The practical HBM read rate: the library's plain read kernel over 1 GiB
+    (16-byte loads, every byte read once), median of `reps` launches."""
+    import torch
+
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.empty(ops.STREAM_SINK_WORDS, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        ops.stream_read(buf, sink)
+    torch.cuda.synchronize()
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ev = [(E(), E()) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        ops.stream_read(buf, sink)
+        b.record()
+    torch.cuda.synchronize()
+    t = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    gbs = nbytes / t / 1e9
+    del buf
+    return {"gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "what": "1 GiB read once with 16-byte loads (attnq8_stream_read), median of 10"}
 
 
 def cpu_baseline(wv, iv):

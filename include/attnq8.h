@@ -224,11 +224,23 @@ int attn_verify_head_greedy(const float* logits, int n_rows, int vocab,
  * and out[2p+1] receive the fp16 bit patterns of the signed bytes (p & 255)
  * and (p >> 8).  out is a device buffer of 131,072 uint16 values.
  *
+ * attnq8_stream_read: a plain read of `bytes` bytes at `buf` with 16-byte
+ * vector loads, the practical read-bandwidth ceiling against which the
+ * attention kernels' HBM rates are also reported.  buf is a device pointer,
+ * 16-byte aligned, and bytes a multiple of 16 (0 is allowed); sink is a
+ * device buffer of ATTNQ8_STREAM_SINK_WORDS uint32 words, each written with
+ * the XOR of the 32-bit words one workgroup read, so the XOR of the sink is
+ * the XOR of every word of the buffer.  Errors: ATTNQ8_EINVAL for a null
+ * buffer (with bytes > 0) or sink, ATTNQ8_EALIGN for a misaligned buffer or
+ * a size that is not a multiple of 16; nothing is launched then.
+ *
  * attnq8_status_string: a static description of a status code.
  * attnq8_last_path: a static per-thread description of the kernel variant,
  * grid and split count the calling thread's last successful call launched.
  * ------------------------------------------------------------------------- */
 int attnq8_selftest_i8_to_f16(uint16_t* out, void* stream);
+#define ATTNQ8_STREAM_SINK_WORDS 1024
+int attnq8_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 const char* attnq8_status_string(int status);
 const char* attnq8_last_path(void);
 

@@ -204,6 +204,17 @@ def test_head_rejects_before_launch(lib, kw, status):
     assert _head(lib, **kw) == status
 
 
+@pytest.mark.parametrize("buf,nbytes,sink,status", [
+    (None, 16, A, _lib.EINVAL),
+    (A, 16, None, _lib.EINVAL),
+    (A + 4, 16, A, _lib.EALIGN),
+    (A, 17, A, _lib.EALIGN),
+    (A, 16, A + 2, _lib.EALIGN),
+])
+def test_stream_read_rejects_before_launch(lib, buf, nbytes, sink, status):
+    assert lib.attnq8_stream_read(buf, nbytes, sink, None) == status
+
+
 def test_selftest_rejects_null(lib):
     assert lib.attnq8_selftest_i8_to_f16(None, None) == _lib.EINVAL
 
