@@ -400,9 +400,6 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
   __shared__ __attribute__((aligned(16))) uint8_t pfrag[2][PB_BYTES];  // [n][hi|lo][lane]
   __shared__ float alpha_s[2][NQ][16];
   __shared__ float2 ml_s[NQ][16];
-  // split fp32 variant: the q lo fragments of the QK waves [n][b][lane]
-  constexpr bool QLO_LDS = false;
-  __shared__ __attribute__((aligned(16))) uint8_t qlo_s[QLO_LDS ? NQ * NB * 1024 : 16];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -466,7 +463,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
   // compiler's wait counting carries no q load into the other waves' loops
   // (a wait placed there for a q register would also wait for every copy).
   const bool qk = wave < nq;  // wave-uniform
-  constexpr int NREG = QF32 && !QLO_LDS ? 2 * NB : NB;
+  constexpr int NREG = QF32 ? 2 * NB : NB;
   float4_t regs[NREG];
 #define QR(k) (__builtin_bit_cast(half8_t, regs[(k)]))
 #pragma unroll
@@ -533,8 +530,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
         lo8[e] = (half_t)(x - (float)hi);
       }
       regs[b] = __builtin_bit_cast(float4_t, hi8);
-      if (QLO_LDS) *(half8_t*)(qlo_s + ((wave * NB + b) * 64 + lane) * 16) = lo8;
-      else if (QF32) regs[NB + b] = __builtin_bit_cast(float4_t, lo8);
+      if (QF32) regs[NB + b] = __builtin_bit_cast(float4_t, lo8);
     }
   } else {
     issue_first(0, 1);
@@ -629,7 +625,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
         half8_t ql[KG];
 #pragma unroll
         for (int j = 0; j < KG; ++j)
-          ql[j] = QLO_LDS ? *(const half8_t*)(qlo_s + ((wave * NB + b0 + j) * 64 + lane) * 16) : QR(NB + b0 + j);
+          ql[j] = QR(NB + b0 + j);
 #pragma unroll
         for (int u = 0; u < 2; ++u)
 #pragma unroll
