@@ -11,11 +11,11 @@
 //            ring of tiles in LDS (direct-to-LDS buffer loads, kCopyLead tiles
 //            in flight); buffer ranges end at the split's last key,
 //            so the ragged last tile reads zeros.
-//   convert  (tile t+1, all waves) K codes -> fp16 MFMA fragments in LDS,
-//            exact; each wave reads its own 32-dim block of V transposed with
-//            the gfx950 ds_read_b64_tr_b8 and keeps dV * code in registers as
-//            an exact fp16 hi + lo pair (dV * code has at most 18 significant
-//            bits; hi is the rounded product, lo the fma residual).
+//   convert  (tile t+1) K codes -> fp16 MFMA fragments in LDS, exact; each
+//            PV wave reads its 32-dim blocks of V transposed with the gfx950
+//            ds_read_b64_tr_b8 and keeps dV * code in registers as an exact
+//            fp16 hi + lo pair (dV * code has at most 18 significant bits; hi
+//            is the rounded product, lo the fma residual).
 //   QK       (tile t, one wave per 16 vectors) S^T = K Q^T on
 //            v_mfma_f32_16x16x32_f16, one 32-dim block per MFMA (q in registers,
 //            split hi + lo when given in fp32 after a per-vector power-of-two
@@ -24,11 +24,13 @@
 //            mask; online softmax in base 2 with a lazily moved reference point;
 //            p split into fp16 hi + lo and handed to every wave through LDS
 //            with the tile's rescale factor.
-//   PV       (tile t-1, all waves) each wave owns one 32-dim block of the
-//            output for its share of the vectors: O^T *= alpha, then
+//   PV       (tile t-1) each PV wave owns 32-dim blocks of the output for
+//            its share of the vectors: O^T *= alpha, then
 //            O^T += V^T P^T as (Vhi,Phi) + (Vlo,Phi) + (Vhi,Plo).
-// PV trails QK by one tile, so the waves that own no vectors and the MFMA
-// work of the output are spread over all four SIMDs of the compute unit.
+// PV trails QK by one tile.  Which waves do QK, PV, the K conversion and the
+// copies depends on the number of vector tiles (Roles below); each role runs
+// its own loop with the same barriers, and the roles are spread so that every
+// SIMD of the compute unit carries both MFMA and VALU work.
 //
 // The accuracy contract of "hip: gfx12 (RDNA4) WMMA kernel for the int8-KV QSA
 // prompt attention" (How: fp16 hi+lo of q and p, fixed summation order, online
