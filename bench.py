@@ -6,9 +6,13 @@ sequential rows) followed by one prompt call (attn_prompt_q8) on the prompt
 chunk (12 Q / 1 KV head, head_dim 256, 32,768-token int8 context, 2,048 causal
 queries).  Inputs are seeded synthetic data resident in HBM before timing, in
 several rotating copies so that the 256 MB Infinity Cache cannot serve
-repeats.  Kernel durations come from HIP events recorded on the library's
-stream around each launch; the GPU is held by a spin kernel while the timed
-launches are queued so that host submission latency does not enter them.
+repeats.  Durations come from HIP events recorded on the library's stream:
+around each whole verify call (attention kernel + reducer, nothing recorded
+between them) and each prompt call, and on alternate steps one more event after
+the attention kernel, which times it alone for its roofline.  The GPU is held by
+a spin kernel while the timed launches are queued so that host submission
+latency does not enter them.  The practical HBM read ceiling (a plain 1 GiB
+read by the library's attnq8_stream_read) is reported beside the 8 TB/s peak.
 
 Prints one JSON line.  Other modes:
   --copy-calibration   run only plain device copies of a known size (for
@@ -65,7 +69,7 @@ def log(msg):
 
 
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources: counter results are valid only for this build."""
+    """Hash of the HIP sources: counter results are valid only for the sources they were taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "attention_int8_quantized_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
@@ -102,7 +106,7 @@ def copy_calibration():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+        print(f"bench.py measures one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
