@@ -27,8 +27,8 @@
 namespace attnq8 {
 
 constexpr int kHeadThreads = 256;
-constexpr int kHeadPerLane = 8;                                // logits per lane per pass
-constexpr int kHeadChunk = kHeadThreads * kHeadPerLane;        // 2,048 logits
+constexpr int kHeadPerLane = 16;                               // logits per lane per pass
+constexpr int kHeadChunk = kHeadThreads * kHeadPerLane;        // 4,096 logits
 constexpr int kHeadMaxBlocks = 256;                            // blocks per row
 constexpr int kHeadNone = 0x7FFFFFFF;                          // no index yet
 constexpr int kHeadMaxRows = 1024;

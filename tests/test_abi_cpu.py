@@ -169,10 +169,10 @@ def test_kv_append_rejects_before_launch(lib, kw, status):
 
 def test_head_workspace_bytes(lib):
     f = lib.attn_verify_head_workspace_bytes
-    # 4,096 bytes of tickets, then 16 bytes per block; 248,320 logits = 122
-    # chunks of 2,048: one chunk per block for 1..16 rows
-    assert f(1, 248320) == 4096 + 122 * 16
-    assert f(5, 248320) == 4096 + 5 * 122 * 16
+    # 4,096 bytes of tickets, then 16 bytes per block; 248,320 logits = 61
+    # chunks of 4,096: one chunk per block for 1..33 rows
+    assert f(1, 248320) == 4096 + 61 * 16
+    assert f(5, 248320) == 4096 + 5 * 61 * 16
     assert f(64, 248320) == 4096 + 64 * 32 * 16   # 2,048 blocks over all rows
     assert f(1, 1) == 4096 + 16
     assert f(0, 100) == 0 and f(3, 0) == 0 and f(1025, 100) == 0
