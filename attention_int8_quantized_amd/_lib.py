@@ -78,7 +78,8 @@ class Attnq8Error(RuntimeError):
 
 def header_functions():
     """Names of the functions include/attnq8.h declares."""
-    text = open(HEADER).read()
+    with open(HEADER) as f:
+        text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(attn\w+)\s*\(", text)))
 

@@ -21,6 +21,22 @@ def _ptr(t: torch.Tensor) -> int:
     return t.data_ptr()
 
 
+def _nbytes(t: torch.Tensor) -> int:
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    return t.numel() * t.element_size()
+
+
+def _out(t: Optional[torch.Tensor], shape, dtype, device, name: str = "out") -> torch.Tensor:
+    """A new output tensor, or the caller's after checking that the kernel's
+    writes fit it exactly."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    if not t.is_cuda or not t.is_contiguous() or t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous {dtype} GPU tensor of shape {tuple(shape)}")
+    return t
+
+
 def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
@@ -72,7 +88,7 @@ def verify_partials(q, k_codes, k_scales, v_codes, v_scales, ctx_len: int, rows_
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     st = lib.attn_verify_q8(_ptr(q), _QTYPES[q.dtype], _ptr(k_codes), _ptr(k_scales),
                             _ptr(v_codes), _ptr(v_scales), hq, hkv, hd, stride, ctx_len, n_rows,
-                            rows_per_group, S, _ptr(workspace), workspace.numel(),
+                            rows_per_group, S, _ptr(workspace), _nbytes(workspace),
                             float(sm_scale), _stream())
     _lib.check("attn_verify_q8", st)
     return workspace, S
@@ -89,10 +105,8 @@ def split_views(workspace: torch.Tensor, n_splits, n_rows, n_q_heads, head_dim):
 
 def reduce_partials(workspace: torch.Tensor, n_rows: int, n_q_heads: int, head_dim: int,
                     n_splits: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    if out is None:
-        out = torch.empty((n_rows, n_q_heads, head_dim), dtype=torch.float32,
-                          device=workspace.device)
-    st = _lib.load().attn_reduce_partials(_ptr(workspace), workspace.numel(), n_rows, n_q_heads,
+    out = _out(out, (n_rows, n_q_heads, head_dim), torch.float32, workspace.device)
+    st = _lib.load().attn_reduce_partials(_ptr(workspace), _nbytes(workspace), n_rows, n_q_heads,
                                           head_dim, n_splits, _ptr(out), _stream())
     _lib.check("attn_reduce_partials", st)
     return out
@@ -113,8 +127,7 @@ def prompt(q, k_codes, k_scales, v_codes, v_scales, q_pos0: int, kv_len: Optiona
     n, hq, hkv, hd, stride = _check_cache(q, k_codes, k_scales, v_codes, v_scales)
     if kv_len is None:
         kv_len = q_pos0 + n
-    if out is None:
-        out = torch.empty((n, hq, hd), dtype=torch.float32, device=q.device)
+    out = _out(out, (n, hq, hd), torch.float32, q.device)
     st = _lib.load().attn_prompt_q8(_ptr(q), _QTYPES[q.dtype], _ptr(k_codes), _ptr(k_scales),
                                     _ptr(v_codes), _ptr(v_scales), hq, hkv, hd, stride, kv_len,
                                     q_pos0, n, float(sm_scale), _ptr(out), _stream())
@@ -150,7 +163,7 @@ def verify_f16kv(q, k, v, ctx_len: int, rows_per_group: int = 0, n_splits: int =
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     st = lib.attn_verify_f16kv(_ptr(q), _QTYPES[q.dtype], _ptr(k), _ptr(v), hq, hkv, hd, stride,
                                ctx_len, n_rows, rows_per_group, S, _ptr(workspace),
-                               workspace.numel(), float(sm_scale), _stream())
+                               _nbytes(workspace), float(sm_scale), _stream())
     _lib.check("attn_verify_f16kv", st)
     return reduce_partials(workspace, n_rows, hq, hd, S, out)
 
@@ -166,7 +179,7 @@ def verify_f16kv_partials(q, k, v, ctx_len: int, rows_per_group: int = 0, n_spli
                                 device=q.device)
     st = _lib.load().attn_verify_f16kv(_ptr(q), _QTYPES[q.dtype], _ptr(k), _ptr(v), hq, hkv, hd,
                                        stride, ctx_len, n_rows, rows_per_group, S, _ptr(workspace),
-                                       workspace.numel(), float(sm_scale), _stream())
+                                       _nbytes(workspace), float(sm_scale), _stream())
     _lib.check("attn_verify_f16kv", st)
     return workspace, S
 
@@ -177,8 +190,7 @@ def prompt_f16kv(q, k, v, q_pos0: int, kv_len: Optional[int] = None, sm_scale: f
     n, hq, hkv, hd, stride = _check_cache16(q, k, v)
     if kv_len is None:
         kv_len = q_pos0 + n
-    if out is None:
-        out = torch.empty((n, hq, hd), dtype=torch.float32, device=q.device)
+    out = _out(out, (n, hq, hd), torch.float32, q.device)
     st = _lib.load().attn_prompt_f16kv(_ptr(q), _QTYPES[q.dtype], _ptr(k), _ptr(v), hq, hkv, hd,
                                        stride, kv_len, q_pos0, n, float(sm_scale), _ptr(out),
                                        _stream())
@@ -237,13 +249,11 @@ def verify_head_greedy(logits: torch.Tensor, workspace: Optional[torch.Tensor] =
     need = head_workspace_bytes(rows, vocab)
     if workspace is None:
         workspace = torch.zeros(need, dtype=torch.uint8, device=logits.device)
-    if token is None:
-        token = torch.empty(rows, dtype=torch.int32, device=logits.device)
-    if top_prob is None:
-        top_prob = torch.empty(rows, dtype=torch.float32, device=logits.device)
+    token = _out(token, (rows,), torch.int32, logits.device, "token")
+    top_prob = _out(top_prob, (rows,), torch.float32, logits.device, "top_prob")
     st = _lib.load().attn_verify_head_greedy(_ptr(logits), rows, vocab, logits.stride(0),
                                              _ptr(token), _ptr(top_prob), _ptr(workspace),
-                                             workspace.numel(), _stream())
+                                             _nbytes(workspace), _stream())
     _lib.check("attn_verify_head_greedy", st)
     return token, top_prob
 
@@ -262,12 +272,9 @@ def stream_read(buf: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Te
     """Read every byte of a contiguous device tensor (its size a multiple of 16
     bytes) with the library's plain read kernel; returns the 1,024-word sink
     whose XOR is the XOR of the buffer's 32-bit words."""
-    if not buf.is_contiguous():
-        raise ValueError("stream_read needs a contiguous tensor")
-    if sink is None:
-        sink = torch.empty(STREAM_SINK_WORDS, dtype=torch.int32, device=buf.device)
-    if sink.numel() * sink.element_size() < 4 * STREAM_SINK_WORDS:
-        raise ValueError("stream_read needs a sink of 1,024 32-bit words")
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("stream_read needs a contiguous GPU tensor")
+    sink = _out(sink, (STREAM_SINK_WORDS,), torch.int32, buf.device, "sink")
     _lib.check("attnq8_stream_read",
                _lib.load().attnq8_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
                                               _stream()))
