@@ -23,6 +23,9 @@ Prints one JSON line.  Other modes:
                        rows, at 24 Q / 4 KV heads, head_dim 256, contexts
                        2,048 / 4,096 / 20,676 / 32,768 and head_dim 128 at
                        8,192; one JSON line per cell
+  --oracle-times       the fp64 oracle per workload on the host (bounded
+                       samples, no GPU) and the tests' pure-Python brute force
+                       on the tiny verify; one JSON line per workload
 """
 
 from __future__ import annotations
@@ -61,6 +64,8 @@ def parse():
     ap.add_argument("--rotate-bytes", type=float, default=1.1e9)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--oracle-times", action="store_true",
+                    help="time the fp64 oracle per workload on the host (no GPU)")
     return ap.parse_args()
 
 
@@ -114,6 +119,9 @@ def main():
         return
     if args.sweep:
         sweep(args)
+        return
+    if args.oracle_times:
+        oracle_times()
         return
 
     import torch
@@ -321,6 +329,72 @@ def read_ceiling(ops, dev, nbytes=1 << 30, reps=10):
     del buf
     return {"gbs": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
             "what": "1 GiB read once with 16-byte loads (attnq8_stream_read), median of 10"}
+
+
+def _host_threads():
+    try:
+        import threadpoolctl
+
+        info = threadpoolctl.threadpool_info()
+        return max([i.get("num_threads", 1) for i in info] or [1])
+    except Exception:
+        return os.cpu_count()
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_times():
+    """The fp64 oracle per workload on the host, each on a bounded sample timed
+    for a few seconds, and the pure-Python brute force of the tests on the tiny
+    verify; one JSON line per workload."""
+    import oracle
+    import workloads as W
+
+    host = {"cpu": _cpu_model(), "cpu_count": os.cpu_count(), "blas_threads": _host_threads()}
+    for name, w in W.WORKLOADS.items():
+        inp = W.generate(w)
+        if w.kind == "verify":
+            # one KV head with its query heads, all rows
+            q = inp.q[:, : w.group]
+            call = lambda: oracle.verify(q, inp.k_codes[:1], inp.k_scales[:1],  # noqa: E731
+                                         inp.v_codes[:1], inp.v_scales[:1], w.ctx_len)
+            frac = 1.0 / w.n_kv_heads
+        else:
+            rows = list(range(0, w.n_queries, max(1, w.n_queries // 16)))
+            call = lambda: oracle.prompt(inp.q, inp.k_codes, inp.k_scales,  # noqa: E731
+                                         inp.v_codes, inp.v_scales, w.pos0, rows=rows)
+            frac = len(rows) / w.n_queries
+        reps, t0 = 0, time.perf_counter()
+        while reps < 1 or (time.perf_counter() - t0 < 3.0 and reps < 1000):
+            call()
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        full_s = dt / frac
+        line = {"mode": "oracle-times", "workload": name, "sample_s": round(dt, 4),
+                "sample_fraction": round(frac, 5), "whole_workload_s": round(full_s, 5),
+                "algorithmic_gflops": round(w.algorithmic_flops() * frac / dt / 1e9, 3), **host}
+        print(json.dumps(line), flush=True)
+    # the pure-Python brute force of the tests on the tiny verify, one core
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import bruteforce
+
+    w = W.TINY_VERIFY
+    inp = W.generate(w)
+    pos = [w.ctx_len + r for r in range(w.n_rows)]
+    t0 = time.perf_counter()
+    bruteforce.attention(inp.q.tolist(), pos, inp.k_codes.tolist(), inp.k_scales.tolist(),
+                         inp.v_codes.tolist(), inp.v_scales.tolist())
+    print(json.dumps({"mode": "oracle-times", "workload": w.name, "brute_force_s":
+                      round(time.perf_counter() - t0, 3), "cores": 1, **host}), flush=True)
 
 
 def cpu_baseline(wv, iv):
