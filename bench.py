@@ -34,6 +34,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -224,7 +225,10 @@ def main():
     kp = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)]) * 1e-3
     step_ms = t_start.elapsed_time(t_end) / K
 
-    vbytes = wv.visible_kv_bytes(args.rows_per_group or None)
+    # KV bytes of the grouping the library used (rows_per_group 0 = its choice)
+    m = re.search(r"rows_per_group(\d+)", verify_path or "")
+    rg_used = int(m.group(1)) if m else (args.rows_per_group or wv.rows_per_group)
+    vbytes = wv.visible_kv_bytes(rg_used)
     verify_s = float(np.mean(kv))
     gbs = vbytes / verify_s / 1e9
     k1_mean = float(np.mean(k1))
@@ -246,8 +250,8 @@ def main():
         "data": "synthetic (seeded N(0,1), int8 block-32 quantised KV)",
         "config": {
             "workload": wv.name,
-            "verify": {**W.describe(wv), "splits": S, "rotating_copies": len(vbufs),
-                       "path": verify_path},
+            "verify": {**W.describe(wv), "rows_per_group": rg_used, "splits": S,
+                       "rotating_copies": len(vbufs), "path": verify_path},
             "parallelism": "single-gpu",
         },
         "verify": {
@@ -522,7 +526,10 @@ def time_f16kv(ops, dev, wv, wp, steps, warmup, with_prompt):
     vcall(0)
     vpath = ops.last_path()
     t = _events_mean(vcall, steps, warmup)
-    vis = wv.visible_kv_bytes() // (2 * (wv.head_dim + wv.head_dim // 16)) * 4 * wv.head_dim
+    # fp16 K and V bytes of the grouping the library chose
+    m = re.search(r"rows_per_group(\d+)", vpath or "")
+    rg = int(m.group(1)) if m else wv.rows_per_group
+    vis = wv.visible_kv_bytes(rg) // (2 * (wv.head_dim + wv.head_dim // 16)) * 4 * wv.head_dim
     out["verify_f16kv"] = {
         "workload": f"{wv.name} over an fp16 cache",
         "path": vpath,
