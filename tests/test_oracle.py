@@ -112,3 +112,15 @@ def test_f16kv_against_brute_force():
         assert np.max(np.abs(got - ref)) <= 1e-12 * np.abs(ref).max()
         with pytest.raises(TypeError):
             oracle.verify_f16kv(q, k.astype(np.float32), v, ctx)
+
+
+def test_golden_files_name_their_source():
+    import os
+
+    golden = os.path.join(os.path.dirname(__file__), "golden")
+    for name in sorted(os.listdir(golden)):
+        if name == "README.md" or name.startswith("."):
+            continue
+        with open(os.path.join(golden, name)) as f:
+            head = f.read(2048)
+        assert "source:" in head.lower(), f"tests/golden/{name} does not name its source"
