@@ -11,6 +11,7 @@
 #include "append_kernel.h"
 #include "attend_kernel.h"
 #include "head_kernel.h"
+#include "prompt_kernel.h"
 #include "stream_kernel.h"
 
 namespace {
@@ -96,7 +97,8 @@ KernelFn pick_nq(int nq) {
     case 2: if constexpr (HD >= 128) return kernel_of<HD, QF32, FINAL, 2, KV16>(); else return nullptr;
     case 3: if constexpr (HD == 256) return kernel_of<HD, QF32, FINAL, 3, KV16>(); else return nullptr;
     case 4: return kernel_of<HD, QF32, FINAL, 4, KV16>();
-    case 6: if constexpr (HD == 256) return kernel_of<HD, QF32, FINAL, 6, KV16>(); else return nullptr;
+    // (the int8 prompt at head_dim 256 and six tiles has a kernel of its own)
+    case 6: if constexpr (HD == 256 && !(FINAL && !KV16)) return kernel_of<HD, QF32, FINAL, 6, KV16>(); else return nullptr;
     // an fp16 ring at head_dim 256 leaves no LDS for eight vector tiles
     case 8: if constexpr (!(KV16 && HD == 256)) return kernel_of<HD, QF32, FINAL, 8, KV16>(); else return nullptr;
     default: return nullptr;
@@ -226,6 +228,10 @@ int prompt_launch(const void* q, int q_dtype, const void* k, const uint16_t* k_s
   if (st) return st;
   const int nq = nq_for(rq * G, head_dim);
   KernelFn fn = pick_kernel<true, KV16>(head_dim, q_dtype == ATTNQ8_F32, nq);
+  // six vector tiles at head_dim 256 over an int8 cache: the layout in which
+  // each compute wave owns its vectors end to end
+  const bool own = !KV16 && head_dim == 256 && nq == 6;
+  if (own) fn = q_dtype == ATTNQ8_F32 ? prompt_own_q8_kernel<true> : prompt_own_q8_kernel<false>;
   if (!fn) return ATTNQ8_EUNSUPPORTED;
   AttendArgs a;
   a.q = q;
@@ -249,8 +255,8 @@ int prompt_launch(const void* q, int q_dtype, const void* k, const uint16_t* k_s
   st = launch_status();
   if (st) return st;
   snprintf(g_last_path, sizeof(g_last_path),
-           "prompt kv%s hd%d q%s tiles%d rows_per_group%d groups%d kv_heads%d", KV16 ? "f16" : "q8",
-           head_dim, q_dtype == ATTNQ8_F32 ? "f32" : "f16", nq, rq, groups, n_kv_heads);
+           "prompt kv%s hd%d q%s tiles%d%s rows_per_group%d groups%d kv_heads%d", KV16 ? "f16" : "q8",
+           head_dim, q_dtype == ATTNQ8_F32 ? "f32" : "f16", nq, own ? " own" : "", rq, groups, n_kv_heads);
   return ATTNQ8_OK;
 }
 }  // namespace

@@ -82,3 +82,33 @@ def test_prompt_first_query_is_value():
     vhat = oracle.dequantize(inp.v_codes[0, 0], inp.v_scales[0, 0])
     for h in range(4):
         assert np.max(np.abs(got[0, h] - vhat)) <= 2.0 ** -21 * np.abs(vhat).max()
+
+
+OWN = [
+    # hq, hkv, hd, kv_len, n_queries, q_pos0 (None = at the end), stride_pad, q dtype: row groups
+    # of 81..96 vectors at head_dim 256 (one compute wave per 16 vectors), ragged last groups
+    (96, 8, 256, 400, 229, None, 0, np.float16),    # 8 rows x 12 heads; last group 5 rows
+    (96, 8, 256, 300, 227, 0, 5, np.float32),       # fp32 q, query 0 at position 0, padded stride
+    (32, 2, 256, 800, 700, None, 0, np.float16),    # 6 rows x 16 heads; last group 4 rows
+    (11, 1, 256, 1900, 1800, None, 0, np.float32),  # 8 rows x 11 heads = 88 vectors
+    (12, 1, 256, 1900, 1795, 17, 0, np.float16),    # last group 3 rows; context past the chunk
+]
+
+
+@pytest.mark.parametrize("case", OWN, ids=lambda c: "-".join(str(x) if not isinstance(x, type) else x.__name__ for x in c))
+def test_own_layout_shapes(case):
+    hq, hkv, hd, kv_len, n, pos0, pad, qd = case
+    w = W.PromptWorkload("own", hq, hkv, hd, kv_len, n, seed=kv_len + 7 * n, q_pos0=pos0,
+                         kv_stride=kv_len + pad)
+    note(f"prompt own layout {case}")
+    inp = W.generate(w)
+    inp.q = inp.q.astype(qd)
+    _, got, path = run_prompt(w, inp)
+    note(f"  path: {path}")
+    assert "tiles6 own" in path
+    # the first and last rows of every row group near the ends, a spread in between
+    rows = sorted(set(list(range(0, 18)) + list(range(n - 18, n)) +
+                      list(np.random.default_rng(n).integers(0, n, 24))))
+    ref = oracle.prompt(inp.q, inp.k_codes, inp.k_scales, inp.v_codes, inp.v_scales, w.pos0,
+                        rows=rows)
+    assert_parity(got[rows], ref, f"prompt own layout {case}")
