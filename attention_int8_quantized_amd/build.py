@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["attnq8.hip"]
-DEPENDS = ["attnq8.hip", "append_kernel.h", "attend_kernel.h", "device_utils.h", "head_kernel.h", "prompt_kernel.h", "stream_kernel.h"]
+DEPENDS = ["attnq8.hip", "append_kernel.h", "attend_kernel.h", "device_utils.h", "head_kernel.h", "own_kernel.h", "stream_kernel.h"]
 
 
 def hipcc() -> str:

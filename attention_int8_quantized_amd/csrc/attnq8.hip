@@ -11,7 +11,7 @@
 #include "append_kernel.h"
 #include "attend_kernel.h"
 #include "head_kernel.h"
-#include "prompt_kernel.h"
+#include "own_kernel.h"
 #include "stream_kernel.h"
 
 namespace {
@@ -97,16 +97,26 @@ KernelFn pick_nq(int nq) {
     case 2: if constexpr (HD >= 128) return kernel_of<HD, QF32, FINAL, 2, KV16>(); else return nullptr;
     case 3: if constexpr (HD == 256) return kernel_of<HD, QF32, FINAL, 3, KV16>(); else return nullptr;
     case 4: return kernel_of<HD, QF32, FINAL, 4, KV16>();
-    // (the int8 prompt at head_dim 256 and six tiles has a kernel of its own)
-    case 6: if constexpr (HD == 256 && !(FINAL && !KV16)) return kernel_of<HD, QF32, FINAL, 6, KV16>(); else return nullptr;
+    // (int8 at head_dim 256 with six tiles: the own layout)
+    case 6: if constexpr (HD == 256 && KV16) return kernel_of<HD, QF32, FINAL, 6, KV16>(); else return nullptr;
     // an fp16 ring at head_dim 256 leaves no LDS for eight vector tiles
     case 8: if constexpr (!(KV16 && HD == 256)) return kernel_of<HD, QF32, FINAL, 8, KV16>(); else return nullptr;
     default: return nullptr;
   }
 }
 
+// Row groups of six vector tiles at head_dim 256 over an int8 cache take the
+// layout in which each compute wave owns its vectors end to end.  (With two or
+// three tiles that layout leaves the SIMDs' MFMA pipes to one wave each and
+// gains nothing over the split roles; those row groups keep the general body.)
+bool own_layout(bool kv16, int hd, int nq) { return !kv16 && hd == 256 && nq == 6; }
+
+template <bool FINAL, bool QF32>
+KernelFn pick_own(int nq) { return nq == 6 ? attend_own_q8_kernel<QF32, FINAL, 6> : nullptr; }
+
 template <bool FINAL, bool KV16 = false>
 KernelFn pick_kernel(int hd, bool qf32, int nq) {
+  if (own_layout(KV16, hd, nq)) return qf32 ? pick_own<FINAL, true>(nq) : pick_own<FINAL, false>(nq);
   switch (hd) {
     case 64: return qf32 ? pick_nq<64, true, FINAL, KV16>(nq) : pick_nq<64, false, FINAL, KV16>(nq);
     case 128: return qf32 ? pick_nq<128, true, FINAL, KV16>(nq) : pick_nq<128, false, FINAL, KV16>(nq);
@@ -193,9 +203,9 @@ int verify_launch(const void* q, int q_dtype, const void* k, const uint16_t* k_s
   st = launch_status();
   if (st) return st;
   snprintf(g_last_path, sizeof(g_last_path),
-           "verify kv%s hd%d q%s tiles%d rows_per_group%d groups%d splits%d kv_heads%d",
-           KV16 ? "f16" : "q8", head_dim, q_dtype == ATTNQ8_F32 ? "f32" : "f16", nq, rg, groups, S,
-           n_kv_heads);
+           "verify kv%s hd%d q%s tiles%d%s rows_per_group%d groups%d splits%d kv_heads%d",
+           KV16 ? "f16" : "q8", head_dim, q_dtype == ATTNQ8_F32 ? "f32" : "f16", nq,
+           own_layout(KV16, head_dim, nq) ? " own" : "", rg, groups, S, n_kv_heads);
   return ATTNQ8_OK;
 }
 
@@ -228,10 +238,7 @@ int prompt_launch(const void* q, int q_dtype, const void* k, const uint16_t* k_s
   if (st) return st;
   const int nq = nq_for(rq * G, head_dim);
   KernelFn fn = pick_kernel<true, KV16>(head_dim, q_dtype == ATTNQ8_F32, nq);
-  // six vector tiles at head_dim 256 over an int8 cache: the layout in which
-  // each compute wave owns its vectors end to end
-  const bool own = !KV16 && head_dim == 256 && nq == 6;
-  if (own) fn = q_dtype == ATTNQ8_F32 ? prompt_own_q8_kernel<true> : prompt_own_q8_kernel<false>;
+  const bool own = own_layout(KV16, head_dim, nq);
   if (!fn) return ATTNQ8_EUNSUPPORTED;
   AttendArgs a;
   a.q = q;

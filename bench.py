@@ -287,7 +287,7 @@ def main():
             "rotating_copies": len(pbufs),
         }
         res["prompt_roofline"] = {
-            "kernel": "prompt_own_q8_kernel (prompt)",
+            "kernel": "attend_own_q8_kernel (prompt)",
             "bound": "mfma",
             "achieved": round(tf, 2),
             "peak": FP16_MFMA_PEAK_TFLOPS,

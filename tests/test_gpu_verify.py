@@ -70,6 +70,8 @@ SMALL = [
     (24, 4, 256, 2000, 8, 0, 63, np.float32, 0),  # every split 1 tile
     (24, 4, 256, 777, 32, 0, 0, np.float32, 5),   # 32 rows: groups of 10, 10, 10, 2
     (24, 4, 256, 777, 32, 0, 0, np.float16, 0),
+    (24, 2, 256, 900, 8, 8, 0, np.float32, 0),    # 96 vectors per group: the own layout
+    (24, 2, 256, 333, 13, 8, 3, np.float16, 2),   # own layout; groups of 8 and 5 rows
 ]
 
 
@@ -83,6 +85,7 @@ def test_small_shapes(case):
     inp.q = inp.q.astype(qd)
     _, got, path = run_verify(w, rows_per_group=rg, n_splits=splits, inp=inp)
     note(f"  path: {path}")
+    assert ("own" in path) == (hd == 256 and "tiles6" in path)
     ref = oracle_verify(inp, w)
     assert_parity(got, ref, f"small {case}")
 

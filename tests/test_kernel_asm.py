@@ -27,7 +27,7 @@ def device_asm(tmp_path_factory):
 
 
 def _kernels(asm):
-    names = re.findall(r"^(_ZN6attnq8\d+(?:attend_\w+|prompt_own_q8)_kernelI\w+AttendArgsE):", asm, re.M)
+    names = re.findall(r"^(_ZN6attnq8\d+attend_\w+_kernelI\w+AttendArgsE):", asm, re.M)
     for n in names:
         start = asm.index(n + ":")
         yield n, asm[start:asm.index(".Lfunc_end", start)].split("\n")
@@ -61,7 +61,7 @@ def test_no_compiler_vmcnt_wait_inside_loops(device_asm):
 def test_no_scratch_in_attention_kernels(device_asm):
     for block in re.split(r"\n  - \.", device_asm.split("amdhsa.kernels:")[1]):
         name = re.search(r"name:\s+(\S+)", block)
-        if not name or ("attend" not in name.group(1) and "prompt_own" not in name.group(1)):
+        if not name or "attend" not in name.group(1):
             continue
         spill = re.search(r"\.vgpr_spill_count:\s+(\d+)", block)
         priv = re.search(r"\.private_segment_fixed_size:\s+(\d+)", block)
