@@ -67,3 +67,23 @@ def test_no_scratch_in_attention_kernels(device_asm):
         priv = re.search(r"\.private_segment_fixed_size:\s+(\d+)", block)
         assert spill and int(spill.group(1)) == 0, name.group(1)
         assert priv and int(priv.group(1)) == 0, name.group(1)
+
+
+def test_m0_is_used_only_by_the_tile_copies(device_asm):
+    """The direct-to-LDS copies set m0 (the LDS destination) in inline assembly,
+    and the compiler warns that it may not preserve a reserved register across
+    such a statement.  That is harmless as long as no compiler-generated
+    instruction reads or writes m0: checked here for every kernel."""
+    names = re.findall(r"^(_ZN6attnq8\w+):", device_asm, re.M)
+    assert names
+    for name in names:
+        start = device_asm.index(name + ":")
+        body = device_asm[start:device_asm.index(".Lfunc_end", start)].split("\n")
+        in_asm = False
+        for line in body:
+            if ";;#ASMSTART" in line:
+                in_asm = True
+            elif ";;#ASMEND" in line:
+                in_asm = False
+            elif not in_asm and re.search(r"\bm0\b", line.split(";")[0]):
+                raise AssertionError(f"{name}: compiler use of m0: {line.strip()}")
