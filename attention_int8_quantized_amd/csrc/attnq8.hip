@@ -97,26 +97,29 @@ KernelFn pick_nq(int nq) {
     case 2: if constexpr (HD >= 128) return kernel_of<HD, QF32, FINAL, 2, KV16>(); else return nullptr;
     case 3: if constexpr (HD == 256) return kernel_of<HD, QF32, FINAL, 3, KV16>(); else return nullptr;
     case 4: return kernel_of<HD, QF32, FINAL, 4, KV16>();
-    // (int8 at head_dim 256 with six tiles: the own layout)
-    case 6: if constexpr (HD == 256 && KV16) return kernel_of<HD, QF32, FINAL, 6, KV16>(); else return nullptr;
+    case 6: return nullptr;  // (head_dim 256 with six tiles: the own layout)
     // an fp16 ring at head_dim 256 leaves no LDS for eight vector tiles
     case 8: if constexpr (!(KV16 && HD == 256)) return kernel_of<HD, QF32, FINAL, 8, KV16>(); else return nullptr;
     default: return nullptr;
   }
 }
 
-// Row groups of six vector tiles at head_dim 256 over an int8 cache take the
-// layout in which each compute wave owns its vectors end to end.  (With two or
-// three tiles that layout leaves the SIMDs' MFMA pipes to one wave each and
+// Row groups of six vector tiles at head_dim 256 take the layout in which each
+// compute wave owns its vectors end to end.  (With two or three tiles over an
+// int8 cache that layout leaves the SIMDs' MFMA pipes to one wave each and
 // gains nothing over the split roles; those row groups keep the general body.)
-bool own_layout(bool kv16, int hd, int nq) { return !kv16 && hd == 256 && nq == 6; }
+bool own_layout(bool kv16, int hd, int nq) { return hd == 256 && nq == 6; }
 
-template <bool FINAL, bool QF32>
-KernelFn pick_own(int nq) { return nq == 6 ? attend_own_q8_kernel<QF32, FINAL, 6> : nullptr; }
+template <bool FINAL, bool QF32, bool KV16>
+KernelFn pick_own(int nq) {
+  if (nq != 6) return nullptr;
+  if constexpr (KV16) return attend_own_f16kv_kernel<QF32, FINAL, 6>;
+  else return attend_own_q8_kernel<QF32, FINAL, 6>;
+}
 
 template <bool FINAL, bool KV16 = false>
 KernelFn pick_kernel(int hd, bool qf32, int nq) {
-  if (own_layout(KV16, hd, nq)) return qf32 ? pick_own<FINAL, true>(nq) : pick_own<FINAL, false>(nq);
+  if (own_layout(KV16, hd, nq)) return qf32 ? pick_own<FINAL, true, KV16>(nq) : pick_own<FINAL, false, KV16>(nq);
   switch (hd) {
     case 64: return qf32 ? pick_nq<64, true, FINAL, KV16>(nq) : pick_nq<64, false, FINAL, KV16>(nq);
     case 128: return qf32 ? pick_nq<128, true, FINAL, KV16>(nq) : pick_nq<128, false, FINAL, KV16>(nq);

@@ -21,7 +21,9 @@
 //
 // LDS: a ring of three int8 stages (a stage is free once its tile has been
 // converted), double-buffered K fragments (16 KB), K scales (512 B) and V^T
-// fragments (32 KB): 151,552 B in all.
+// fragments (32 KB): 151,552 B in all.  Over an fp16 cache nothing is
+// converted: the compute waves read K and V^T fragments from a ring of four
+// 32 KB stages, and the two feeders only copy.
 //
 // Per iteration t (one workgroup barrier each): the copying feeders have waited
 // for their copies of tile t+1; after the barrier they copy tile t+3 into the
@@ -180,17 +182,49 @@ __device__ __forceinline__ void own_feed(const AttendArgs& a, size_t head_rows, 
   wait_vmcnt<0>();  // copies past the last tile may still be landing
 }
 
-template <bool QF32, bool FINAL, int NQ>
-__global__ __launch_bounds__(64 * kWaves) void attend_own_q8_kernel(const AttendArgs a) {
+// The feeders' loop over an fp16 cache (no conversion: the compute waves read
+// K and V^T fragments from the ring): iteration t waits for this feeder's
+// copies of tile t, passes the barrier and copies tile t+D-1 into the stage of
+// tile t-1.  Feeder F of NF takes code chunks F, F + NF, ... of each plane.
+template <int NF, int F, int D>
+__device__ __forceinline__ void own_feed16(const AttendArgs& a, size_t head_rows, int k_end, int t_begin, int t_end,
+                                           int lane, uint32_t ring0) {
+  using L = Stage16<256>;
+  TileCopier<L, NF> cp;
+  cp.kc = make_rsrc((const uint8_t*)a.kc + head_rows * L::ROW, k_end * L::ROW);
+  cp.vc = make_rsrc((const uint8_t*)a.vc + head_rows * L::ROW, k_end * L::ROW);
+  cp.init(F, lane);
+  cp.issue(ring0, t_begin * 32, t_begin < t_end);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();  // q goes out with the first tile, the other tiles after
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int s = 1; s < D - 1; ++s) cp.issue(ring0 + s * L::BYTES, (t_begin + s) * 32, t_begin + s < t_end);
+  int slot = D - 1;  // ring stage of tile t + D - 1
+  for (int t = t_begin; t < t_end; ++t) {
+    cp.template wait_all_but<D - 2>();
+    __syncthreads();  // tile t landed; tile t-1 consumed
+    cp.issue(ring0 + slot * L::BYTES, (t + D - 1) * 32, t + D - 1 < t_end);
+    slot = slot + 1 == D ? 0 : slot + 1;
+  }
+  wait_vmcnt<0>();  // copies past the last tile may still be landing
+}
+
+template <bool QF32, bool FINAL, int NQ, bool KV16>
+__device__ __forceinline__ void attend_own_body(const AttendArgs& a) {
   constexpr int HD = 256;
-  using L = Stage<HD>;
+  using L = std::conditional_t<KV16, Stage16<HD>, Stage<HD>>;
   constexpr int NB = L::NB;                    // 32-dim blocks
   constexpr int NDT = HD / 16;                 // 16-dim output tiles
   constexpr int NF = kWaves - NQ;              // feeding waves
-  constexpr int D = 3;                         // ring stages
-  constexpr int KF_BYTES = NB * 2 * 1024;      // K fragments [b][u][lane]
-  constexpr int VF_BYTES = NDT * 2 * 1024;     // V^T fragments [d][hi|lo][lane]
-  constexpr int KS_BYTES = 32 * NB * 2;        // K scales [key][b]
+  // ring stages: an int8 stage is free once converted (tiles t+1 .. t+3 in it);
+  // an fp16 stage is read in place (tiles t .. t+3)
+  constexpr int D = KV16 ? 4 : 3;
+  // converted K fragments [b][u][lane], V^T fragments [d][hi|lo][lane] and K
+  // scales [key][b] (int8 only)
+  constexpr int KF_BYTES = KV16 ? 16 : NB * 2 * 1024;
+  constexpr int VF_BYTES = KV16 ? 16 : NDT * 2 * 1024;
+  constexpr int KS_BYTES = KV16 ? 16 : 32 * NB * 2;
   static_assert(NQ >= 2 && NQ <= 6, "two to six compute waves");
   static_assert(D * L::BYTES + 2 * (KF_BYTES + VF_BYTES + KS_BYTES) <= 160 * 1024, "LDS");
 
@@ -236,13 +270,19 @@ __global__ __launch_bounds__(64 * kWaves) void attend_own_q8_kernel(const Attend
   if (wave >= NQ) {
     // ---- feeders (each specialised by its index, so that its shares are
     // compile-time)
-    switch (wave - NQ) {
-      case 0: own_feed<NF, 0, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
-      case 1: if constexpr (NF > 1) own_feed<NF, 1, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
-      case 2: if constexpr (NF > 2) own_feed<NF, 2, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
-      case 3: if constexpr (NF > 3) own_feed<NF, 3, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
-      case 4: if constexpr (NF > 4) own_feed<NF, 4, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
-      default: if constexpr (NF > 5) own_feed<NF, 5, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
+    if constexpr (KV16) {
+      static_assert(NF == 2, "copy-only feeders: two");
+      if (wave == NQ) own_feed16<NF, 0, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_.ring0);
+      else own_feed16<NF, 1, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_.ring0);
+    } else {
+      switch (wave - NQ) {
+        case 0: own_feed<NF, 0, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
+        case 1: if constexpr (NF > 1) own_feed<NF, 1, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
+        case 2: if constexpr (NF > 2) own_feed<NF, 2, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
+        case 3: if constexpr (NF > 3) own_feed<NF, 3, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
+        case 4: if constexpr (NF > 4) own_feed<NF, 4, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
+        default: if constexpr (NF > 5) own_feed<NF, 5, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
+      }
     }
     return;
   }
@@ -336,15 +376,36 @@ __global__ __launch_bounds__(64 * kWaves) void attend_own_q8_kernel(const Attend
 #pragma unroll
   for (int d = 0; d < NDT; ++d) O[d] = (float4_t){0, 0, 0, 0};
 
-  // tile t from buffer t & 1
-  auto own_tile = [&](int t) {
+  // tile t from buffer t & 1 (an fp16 cache: from its ring stage `st`)
+  auto own_tile = [&](int t, const uint8_t* st) {
     const int key0 = t * 32;
     const uint8_t* kf = kfrag[t & 1];
     const half_t* Kst = (const half_t*)kscale[t & 1];
     // S^T = K Q^T, two blocks at a time for both 16-key subtiles: the hi MFMAs,
-    // the lo MFMAs, then the per-block K scales in fp32, in block order
+    // the lo MFMAs, then the per-block K scales in fp32, in block order (an fp16
+    // K has no scales: every block accumulates into S^T, in block order)
     constexpr int KG = 2;
     float4_t s[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+    if constexpr (KV16) {
+#pragma unroll
+      for (int b0 = 0; b0 < NB; b0 += KG) {
+        half8_t kv[2][KG];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int j = 0; j < KG; ++j) {
+            const int key = 16 * u + n16;
+            kv[u][j] = *(const half8_t*)(st + L::K_OFF + key * L::ROW + 16 * L::slot(key, 4 * (b0 + j) + h4));
+          }
+#pragma unroll
+        for (int j = 0; j < KG; ++j)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            s[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv[u][j], QR(b0 + j), s[u], 0, 0, 0);
+            if (QF32) s[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kv[u][j], QR(NB + b0 + j), s[u], 0, 0, 0);
+          }
+      }
+    } else {
 #pragma unroll
     for (int b0 = 0; b0 < NB; b0 += KG) {
       half8_t kv[2][KG];
@@ -375,6 +436,7 @@ __global__ __launch_bounds__(64 * kWaves) void attend_own_q8_kernel(const Attend
         for (int j = 0; j < KG; ++j)
 #pragma unroll
           for (int e = 0; e < 4; ++e) s[u][e] = fmaf((float)dk[u][e].get(j), acc[u][j][e], s[u][e]);
+    }
     }
     // mask and online softmax (base 2) on the unscaled dots (xmul > 0)
     float x[2][4];
@@ -429,6 +491,25 @@ __global__ __launch_bounds__(64 * kWaves) void attend_own_q8_kernel(const Attend
 #pragma unroll
       for (int d = 0; d < NDT; ++d) O[d] *= alpha;
     }
+    if constexpr (KV16) {
+      // O^T += (V,Phi) + (V,Plo) (an fp16 V is exact), two blocks at a time
+#pragma unroll
+      for (int b0 = 0; b0 < NB; b0 += 2) {
+        half8_t vh8[2][2];
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) read_v16<HD>(b0 + jb, st, lane, vh8[jb]);
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+          for (int dd = 0; dd < 2; ++dd)
+            O[2 * (b0 + jb) + dd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh8[jb][dd], phi, O[2 * (b0 + jb) + dd], 0, 0, 0);
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+          for (int dd = 0; dd < 2; ++dd)
+            O[2 * (b0 + jb) + dd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh8[jb][dd], plo, O[2 * (b0 + jb) + dd], 0, 0, 0);
+      }
+    } else {
     // O^T += (Vhi,Phi) + (Vlo,Phi) + (Vhi,Plo), four output tiles at a time
     const uint8_t* vf = vfrag[t & 1];
 #pragma unroll
@@ -446,13 +527,23 @@ __global__ __launch_bounds__(64 * kWaves) void attend_own_q8_kernel(const Attend
 #pragma unroll
       for (int i = 0; i < 4; ++i) O[d0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh8[i], plo, O[d0 + i], 0, 0, 0);
     }
+    }
   };
 
   // the same barriers as the feeders' loop: iteration t_begin - 1 converts the
   // first tile
-  for (int t = t_begin - 1; t < t_end; ++t) {
-    __syncthreads();
-    if (own && t >= t_begin) own_tile(t);
+  if constexpr (KV16) {
+    int slot = 0;  // ring stage of tile t
+    for (int t = t_begin; t < t_end; ++t) {
+      __syncthreads();
+      if (own) own_tile(t, ring + slot * L::BYTES);
+      slot = slot + 1 == D ? 0 : slot + 1;
+    }
+  } else {
+    for (int t = t_begin - 1; t < t_end; ++t) {
+      __syncthreads();
+      if (own && t >= t_begin) own_tile(t, nullptr);
+    }
   }
 
   // ---- output of the wave's vectors
@@ -475,6 +566,17 @@ __global__ __launch_bounds__(64 * kWaves) void attend_own_q8_kernel(const Attend
     }
   }
 #undef QR
+}
+
+template <bool QF32, bool FINAL, int NQ>
+__global__ __launch_bounds__(64 * kWaves) void attend_own_q8_kernel(const AttendArgs a) {
+  attend_own_body<QF32, FINAL, NQ, false>(a);
+}
+
+// The same layout over an fp16 K/V cache (no scales, no conversion).
+template <bool QF32, bool FINAL, int NQ>
+__global__ __launch_bounds__(64 * kWaves) void attend_own_f16kv_kernel(const AttendArgs a) {
+  attend_own_body<QF32, FINAL, NQ, true>(a);
 }
 
 }  // namespace attnq8

@@ -41,6 +41,8 @@ SMALL = [
     (64, 1, 128, 70, 2, 0, 0, np.float32, 0),   # 128 vectors in one group
     (24, 4, 256, 2000, 8, 0, 63, np.float32, 0),
     (48, 1, 256, 300, 2, 0, 0, np.float16, 5),  # 96 vectors: the largest group at hd 256
+    (24, 2, 256, 400, 8, 8, 0, np.float32, 0),   # 96 vectors per group: the own layout
+    (24, 2, 256, 333, 13, 8, 3, np.float16, 2),  # own layout; groups of 8 and 5 rows
 ]
 
 
@@ -54,7 +56,9 @@ def test_verify_f16kv_small(case):
     inp.q = inp.q.astype(qd)
     q, k, v = _dev(inp)
     got = ops.verify_f16kv(q, k, v, ctx_len=ctx, rows_per_group=rg, n_splits=splits).cpu().numpy()
-    note(f"  path: {ops.last_path()}")
+    path = ops.last_path()
+    note(f"  path: {path}")
+    assert ("own" in path) == (hd == 256 and "tiles6" in path)
     ref = oracle.verify_f16kv(inp.q, inp.k, inp.v, ctx)
     assert_parity(got, ref, f"small {case}")
 
@@ -92,3 +96,25 @@ def test_f16kv_group_limit_at_256():
     q, k, v = _dev(inp)
     with pytest.raises(Exception):
         ops.verify_f16kv(q, k, v, ctx_len=100, rows_per_group=2)  # 128 vectors > 96
+
+
+@pytest.mark.parametrize("hq,hkv,hd,kv_len,n,pos0,qd", [
+    (96, 8, 256, 400, 229, None, np.float16),   # 8 rows x 12 heads; last group 5 rows
+    (11, 1, 256, 1900, 1800, None, np.float32),  # 8 rows x 11 heads = 88 vectors
+    (32, 2, 256, 800, 700, 3, np.float16),       # 6 rows x 16 heads; context past the chunk
+])
+def test_prompt_f16kv_own_layout(hq, hkv, hd, kv_len, n, pos0, qd):
+    """Row groups of six vector tiles at head_dim 256 take the own layout."""
+    w = W.PromptWorkload("p16own", hq, hkv, hd, kv_len, n, seed=kv_len + 3 * n, q_pos0=pos0)
+    note(f"prompt fp16 cache own layout {hq}/{hkv} hd{hd} kv{kv_len} n{n} {qd.__name__}")
+    inp = W.generate_f16kv(w)
+    inp.q = inp.q.astype(qd)
+    q, k, v = _dev(inp)
+    got = ops.prompt_f16kv(q, k, v, q_pos0=w.pos0, kv_len=w.kv_len).cpu().numpy()
+    path = ops.last_path()
+    note(f"  path: {path}")
+    assert "tiles6 own" in path
+    rows = sorted(set(list(range(0, 18)) + list(range(n - 18, n)) +
+                      list(np.random.default_rng(n).integers(0, n, 24))))
+    ref = oracle.prompt_f16kv(inp.q, inp.k, inp.v, w.pos0, rows=rows)
+    assert_parity(got[rows], ref, "prompt fp16 cache own layout")
