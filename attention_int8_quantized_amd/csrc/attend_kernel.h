@@ -340,35 +340,21 @@ struct Roles {
   static constexpr int PV0 = SPLIT ? 4 : 0;  // first PV wave
   static constexpr int NPV = NW - PV0;       // PV waves
   static constexpr int NB = Stage<HD>::NB;
-  // Six vector tiles at head_dim 256 (a prompt block of 8 queries x 12 heads):
-  // the QK waves 0..5 sit two per SIMD on SIMDs 0 and 1 and one per SIMD on 2
-  // and 3, so the blocks go 0, 0, 1, 1, 1, 1, 2, 2 to waves 0..7 and waves 0
-  // and 1 convert K instead.
-  static constexpr bool UNEVEN = !SPLIT && NQ == 6 && NB == 8;
-  static constexpr int BPW = UNEVEN ? 2 : (NB > NPV ? NB / NPV : 1);  // PV blocks per wave (most)
+  static_assert(NQ == 2 || NQ == 3 || NQ == 4 || NQ == 8, "vector tiles per workgroup");
+  static constexpr int BPW = NB > NPV ? NB / NPV : 1;  // PV blocks per wave
   static constexpr int GW = NPV > NB ? NPV / NB : 1;   // PV waves sharing one block
   static constexpr int NQW = NQ / GW;                  // vector tiles per PV wave
   static_assert(NQ % GW == 0, "vector tiles must split evenly over the waves");
   // PV block j of wave `wave` (NB: none)
-  __device__ static int block(int wave, int j) {
-    if (UNEVEN) {
-      if (wave < 2) return NB;
-      if (wave < 6) return j == 0 ? wave - 2 : NB;
-      return 4 + 2 * (wave - 6) + j;
-    }
-    return wave >= PV0 ? (wave - PV0) % NB + NPV * j : NB;
-  }
+  __device__ static int block(int wave, int j) { return wave >= PV0 ? (wave - PV0) % NB + NPV * j : NB; }
   // first vector tile of the wave's PV share (then every GW-th)
   __device__ static int qtile0(int wave) { return (wave - PV0) / NB; }
   // waves that issue the tile copies, and this wave's index among them (< 0: none)
   static constexpr int NWI = NPV;
   __device__ static int copy_index(int wave) { return wave - PV0; }
   // waves that convert K, and this wave's index among them (< 0: none)
-  __device__ static int k_workers(int nq) { return SPLIT && nq < 4 ? 1 : (UNEVEN ? 2 : NPV); }
-  __device__ static int k_index(int wave, int nq) {
-    if (UNEVEN) return wave < 2 ? wave : -1;
-    return SPLIT && nq < 4 ? (wave == 3 ? 0 : -1) : wave - PV0;
-  }
+  __device__ static int k_workers(int nq) { return SPLIT && nq < 4 ? 1 : NPV; }
+  __device__ static int k_index(int wave, int nq) { return SPLIT && nq < 4 ? (wave == 3 ? 0 : -1) : wave - PV0; }
 };
 
 // HD: head dim; QF32: q given in fp32 (else fp16); FINAL: write the normalised
@@ -581,7 +567,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
     // S^T = K Q^T, KG blocks at a time for both 16-key subtiles: K fragments
     // and key scales first, then the hi MFMAs and the lo MFMAs (each block has
     // its own accumulator), then the per-block K scales in fp32, in block order
-    constexpr int KG = NB < 4 ? NB : (R::SPLIT || R::UNEVEN ? 2 : 4);  // blocks per group (registers)
+    constexpr int KG = NB < 4 ? NB : (R::SPLIT ? 2 : 4);  // blocks per group (registers)
     const half_t* Kst = (const half_t*)(st + L::KS_OFF);
     float4_t s[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
     if constexpr (KV16) {
@@ -981,21 +967,8 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
     };
     using T_ = std::true_type;
     using F_ = std::false_type;
-    if constexpr (R::UNEVEN) {
-      if (wave < 2) {
-        float4_t Oa[1][NQW][2];  // (no blocks: never multiplied)
-        role_loop(T_(), T_(), Oa);
-      } else if (wave < 6) {
-        float4_t Oa[1][NQW][2];
-        role_loop(T_(), F_(), Oa);
-      } else {
-        float4_t Oa[2][NQW][2];
-        role_loop(F_(), F_(), Oa);
-      }
-    } else {
-      float4_t Oa[BPW][NQW][2];
-      role_loop(T_(), T_(), Oa);
-    }
+    float4_t Oa[BPW][NQW][2];
+    role_loop(T_(), T_(), Oa);
   }
 #undef QR
 }
