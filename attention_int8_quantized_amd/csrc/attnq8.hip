@@ -108,13 +108,12 @@ KernelFn pick_nq(int nq) {
 // compute wave owns its vectors end to end.  (With two or three tiles over an
 // int8 cache that layout leaves the SIMDs' MFMA pipes to one wave each and
 // gains nothing over the split roles; those row groups keep the general body.)
-bool own_layout(bool kv16, int hd, int nq) { return hd == 256 && nq == 6; }
+bool own_layout(bool kv16, int hd, int nq) { return hd == 256 && (nq == 6 || (kv16 && nq == 3)); }
 
 template <bool FINAL, bool QF32, bool KV16>
 KernelFn pick_own(int nq) {
-  if (nq != 6) return nullptr;
-  if constexpr (KV16) return attend_own_f16kv_kernel<QF32, FINAL, 6>;
-  else return attend_own_q8_kernel<QF32, FINAL, 6>;
+  if constexpr (KV16) return nq == 6 ? attend_own_f16kv_kernel<QF32, FINAL, 6> : attend_own_f16kv_kernel<QF32, FINAL, 3>;
+  else return nq == 6 ? attend_own_q8_kernel<QF32, FINAL, 6> : nullptr;
 }
 
 template <bool FINAL, bool KV16 = false>

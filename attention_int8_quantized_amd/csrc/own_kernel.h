@@ -271,9 +271,13 @@ __device__ __forceinline__ void attend_own_body(const AttendArgs& a) {
     // ---- feeders (each specialised by its index, so that its shares are
     // compile-time)
     if constexpr (KV16) {
-      static_assert(NF == 2, "copy-only feeders: two");
-      if (wave == NQ) own_feed16<NF, 0, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_.ring0);
-      else own_feed16<NF, 1, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_.ring0);
+      // two waves copy; any others only keep the barriers
+      if (wave == NQ) own_feed16<2, 0, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_.ring0);
+      else if (wave == NQ + 1) own_feed16<2, 1, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_.ring0);
+      else {
+        __builtin_amdgcn_s_barrier();
+        for (int t = t_begin; t < t_end; ++t) __syncthreads();
+      }
     } else {
       switch (wave - NQ) {
         case 0: own_feed<NF, 0, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;

@@ -55,10 +55,12 @@ def test_verify_f16kv_small(case):
     inp = W.generate_f16kv(w)
     inp.q = inp.q.astype(qd)
     q, k, v = _dev(inp)
-    got = ops.verify_f16kv(q, k, v, ctx_len=ctx, rows_per_group=rg, n_splits=splits).cpu().numpy()
-    path = ops.last_path()
+    ws, S = ops.verify_f16kv_partials(q, k, v, ctx_len=ctx, rows_per_group=rg, n_splits=splits)
+    path = ops.last_path()  # the attention kernel's (the reducer records its own)
+    got = ops.reduce_partials(ws, rows, hq, hd, S).cpu().numpy()
     note(f"  path: {path}")
-    assert ("own" in path) == (hd == 256 and "tiles6" in path)
+    assert path.startswith("verify kvf16")
+    assert ("own" in path) == (hd == 256 and ("tiles6" in path or "tiles3" in path))
     ref = oracle.verify_f16kv(inp.q, inp.k, inp.v, ctx)
     assert_parity(got, ref, f"small {case}")
 

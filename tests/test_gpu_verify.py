@@ -17,9 +17,14 @@ def run_verify(w, rows_per_group=0, n_splits=0, q_dtype=None, inp=None):
     if q_dtype is not None:
         inp.q = inp.q.astype(q_dtype)
     dev = to_device(inp)
-    out = ops.verify(*dev, ctx_len=w.ctx_len, rows_per_group=rows_per_group, n_splits=n_splits)
+    # the attention launch and the reducer separately, so that the returned path
+    # is the attention kernel's (the library records the last launch)
+    ws, S = ops.verify_partials(*dev, ctx_len=w.ctx_len, rows_per_group=rows_per_group,
+                                n_splits=n_splits)
+    path = ops.last_path()
+    out = ops.reduce_partials(ws, inp.q.shape[0], inp.q.shape[1], inp.q.shape[2], S)
     torch.cuda.synchronize()
-    return inp, out.cpu().numpy(), ops.last_path()
+    return inp, out.cpu().numpy(), path
 
 
 def oracle_verify(inp, w):
@@ -85,6 +90,7 @@ def test_small_shapes(case):
     inp.q = inp.q.astype(qd)
     _, got, path = run_verify(w, rows_per_group=rg, n_splits=splits, inp=inp)
     note(f"  path: {path}")
+    assert path.startswith("verify kvq8")
     assert ("own" in path) == (hd == 256 and "tiles6" in path)
     ref = oracle_verify(inp, w)
     assert_parity(got, ref, f"small {case}")
