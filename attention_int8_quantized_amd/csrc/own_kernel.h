@@ -1,7 +1,8 @@
-// Attention over an int8 cache at head_dim 256 in a layout in which each
-// compute wave owns 16 query vectors end to end (the library launches it for
-// row groups of six vector tiles, such as the prompt chunk's 8 queries x 12
-// heads; the body also takes two to five compute waves).
+// Attention at head_dim 256 in a layout in which each compute wave owns 16
+// query vectors end to end.  The library launches it for row groups of six
+// vector tiles (such as the prompt chunk's 8 queries x 12 heads) over an int8
+// or fp16 cache, and over an fp16 cache also for three (the verify window's
+// 8 rows x 6 heads); the body takes two to six compute waves.
 //
 // Waves 0..NQ-1 each own one vector tile: per 32-key tile they compute
 // S^T = K Q^T, the mask and the online softmax, and then O^T += V^T P^T over all
@@ -17,7 +18,8 @@
 //
 // With six tiles, SIMDs 0 and 1 carry two compute waves each and SIMDs 2 and 3
 // one compute wave and one feeding wave; with three, SIMDs 0..2 carry one
-// compute wave and one feeding wave each and SIMD 3 two feeding waves.
+// compute wave and one other wave each and SIMD 3 two other waves (over an fp16
+// cache two of the five copy and three only keep the barriers).
 //
 // LDS: a ring of three int8 stages (a stage is free once its tile has been
 // converted), double-buffered K fragments (16 KB), K scales (512 B) and V^T
