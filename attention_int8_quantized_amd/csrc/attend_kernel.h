@@ -15,7 +15,8 @@
 //            PV wave reads its 32-dim blocks of V transposed with the gfx950
 //            ds_read_b64_tr_b8 and keeps dV * code in registers as an exact
 //            fp16 hi + lo pair (dV * code has at most 18 significant bits; hi
-//            is the rounded product, lo the fma residual).
+//            is the rounded product, lo the fma residual; a block with a V
+//            scale above 512 takes a power-of-two shift, undone in fp32).
 //   QK       (tile t, one wave per 16 vectors) S^T = K Q^T on
 //            v_mfma_f32_16x16x32_f16, one 32-dim block per MFMA (q in registers,
 //            split hi + lo when given in fp32 after a per-vector power-of-two
@@ -35,8 +36,10 @@
 // The accuracy contract of "hip: gfx12 (RDNA4) WMMA kernel for the int8-KV QSA
 // prompt attention" (How: fp16 hi+lo of q and p, fixed summation order, online
 // softmax, V scale folded into p) is kept in substance; the V scale is folded
-// into an exact hi+lo V fragment instead of into p, which keeps the fold exact
-// for any scale magnitude.
+// into an exact hi+lo V fragment instead of into p (converted once per tile
+// for all of the workgroup's vectors).  The fold is exact for V scales up to
+// 512; a block of a tile with a larger scale is folded with a power-of-two
+// shift that the PV step undoes in fp32 (see kVScaleFoldMax).
 //
 // The workgroup writes either split partials (m, l, o) or, when it covers every
 // key its rows see, the normalised output.
@@ -269,10 +272,74 @@ __device__ __forceinline__ void convert_k(int b, int u, const uint8_t* st, uint8
   *(half8_t*)(kf + ((b * 2 + u) * 64 + lane) * 16) = codes8_to_f16(w.x, w.y);
 }
 
+// The V-scale fold.  The V^T fragments hold dV * code as an exact fp16 hi + lo
+// pair: with |code| <= 127 the product has at most 18 significant bits, and
+// while |dV| <= 512 its magnitude stays at most 65,024, inside fp16's range;
+// every bit of it lies at or above dV's last bit, so the pair is exact down to
+// fp16's subnormal scales.  A block of a tile that holds a larger scale (the
+// Q8 format allows any fp16 scale: blocks whose largest element exceeds about
+// 65,024 in magnitude) takes a shift s, the smallest with
+// max |dV| * 2^-s <= 512: its scales are multiplied by 2^-s in fp16 (exact
+// for every scale of at least 2^(s-14); a smaller one in such a block is
+// rounded to fp16's subnormal step), the fragments hold
+// (dV * 2^-s) * code, and the PV step brackets that tile's MFMAs for the block
+// with O *= 2^-s and O *= 2^s (fold_scale; exact in fp32: the sum is taken in
+// units of 2^s, with the same roundings relative to its magnitude).
+constexpr uint16_t kVScaleFoldMax = 0x6000;  // 512.0 in fp16
+
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+
+// Whether this lane's eight V scales include one above 512 in magnitude (or a
+// negative, infinite or NaN one: every sign-bit pattern compares above).
+__device__ __forceinline__ bool v_scales_large(half8_t sc) {
+  const u16x8_t b = __builtin_bit_cast(u16x8_t, sc);
+  const u16x4_t m4 = __builtin_elementwise_max(b.lo, b.hi);
+  const u16x2_t m2 = __builtin_elementwise_max(m4.lo, m4.hi);
+  return (m2.x > kVScaleFoldMax) | (m2.y > kVScaleFoldMax);
+}
+
+// The fold shift of a block (wave-uniform) from the scales of the tile's 32
+// keys (each 16-lane group holds those of eight keys pi(h4, e)); when it is
+// not 0 the scales are multiplied by 2^-s in place.
+__device__ __forceinline__ int v_fold_prescale(half8_t& sc) {
+  if (__builtin_expect(!__any(v_scales_large(sc)), 1)) return 0;
+  float mx = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf((float)sc[e]));
+  mx = wave_max_groups(mx);
+  int ex = 0;
+  (void)frexpf(mx, &ex);  // mx < 2^ex
+  const int s = min(15, max(0, ex - 9));
+  sc = sc * (half_t)ldexpf(1.0f, -s);  // 2^-s, s <= 15, is an fp16 value
+  return s;
+}
+
+// O *= 2^(sign * s) for the accumulators O[jb][..][..] of each block jb with a
+// shifted V fold: before a tile's PV MFMAs (sign -1) the block's sum is taken
+// in units of 2^s, after them (sign +1) it returns to the plain units.
+// Scaling by a power of two is exact in fp32 and commutes with the rescale by
+// alpha, so the order of the two does not change a bit.
+template <class Acc, int NBL>
+__device__ __forceinline__ void fold_scale(Acc& O, const int (&sh)[NBL], int sign) {
+#pragma unroll
+  for (int jb = 0; jb < NBL; ++jb) {
+    const float f = ldexpf(1.0f, sign * sh[jb]);
+    constexpr int NI = std::extent<std::remove_reference_t<decltype(O[0])>>::value;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      O[jb][i][0] *= f;
+      O[jb][i][1] *= f;
+    }
+  }
+}
+
 // V codes of block b (dim tiles 2b, 2b+1) of the ring stage `st`, times their
 // per-key scales -> V^T fragments as exact fp16 hi + lo pairs in registers.
+// Returns the block's fold shift (wave-uniform; 0 unless a scale exceeds 512).
 template <int HD>
-__device__ __forceinline__ void convert_v(int b, const uint8_t* st, int lane, half8_t (&vh)[2], half8_t (&vl)[2]) {
+__device__ __forceinline__ int convert_v(int b, const uint8_t* st, int lane, half8_t (&vh)[2], half8_t (&vl)[2]) {
   using L = Stage<HD>;
   constexpr int NB = L::NB;
   const int h4 = lane >> 4;
@@ -284,6 +351,7 @@ __device__ __forceinline__ void convert_v(int b, const uint8_t* st, int lane, ha
   // transposing reads: lane 16h + 2k + s addresses key pi(h, k), dims 16d + 8s
   const int vkey = pi_key(h4, (lane & 15) >> 1);
   const uint8_t* vrow = st + L::V_OFF + vkey * HD + 8 * (lane & 1);
+  const int s = v_fold_prescale(sc);
 #pragma unroll
   for (int dd = 0; dd < 2; ++dd) {
     const v2i32_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
@@ -292,6 +360,7 @@ __device__ __forceinline__ void convert_v(int b, const uint8_t* st, int lane, ha
     vh[dd] = c * sc;
     vl[dd] = __builtin_elementwise_fma(c, sc, -vh[dd]);
   }
+  return s;
 }
 
 // V of block b (dim tiles 2b, 2b+1) of an fp16 ring stage -> V^T fragments
@@ -699,11 +768,16 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
     constexpr int NBL = std::extent<std::remove_reference_t<decltype(Oa)>>::value;
     constexpr int PG = NBL > 1 ? 2 : (NQW < 4 ? NQW : 4);  // vector tiles per group (registers)
     half8_t vh[NBL][2], vl[NBL][2];
+    int vsh[NBL];  // fold shifts of the blocks (wave-uniform)
+    int any_sh = 0;
 #pragma unroll
     for (int jb = 0; jb < NBL; ++jb) {
+      vsh[jb] = 0;
       if constexpr (KV16) read_v16<HD>(R::block(wave, jb), st, lane, vh[jb]);
-      else convert_v<HD>(R::block(wave, jb), st, lane, vh[jb], vl[jb]);
+      else vsh[jb] = convert_v<HD>(R::block(wave, jb), st, lane, vh[jb], vl[jb]);
+      any_sh |= vsh[jb];
     }
+    if (any_sh) fold_scale(Oa, vsh, -1);
     const uint8_t* pf = pfrag[t & 1];
 #pragma unroll
     for (int i0 = 0; i0 < NQW; i0 += PG) {
@@ -750,6 +824,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
         }
       }
     }
+    if (any_sh) fold_scale(Oa, vsh, 1);
   };
 
   // Iteration t: barrier; copy tile t+D-2; QK of tile t; PV of tile t-1;
@@ -793,6 +868,10 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
 #pragma unroll
         for (int i = 0; i < NQW; ++i) O[jb][i][0] = O[jb][i][1] = (float4_t){0, 0, 0, 0};
       half8_t vch[BPW][2], vcl[BPW][2];
+      int vcs[BPW];   // fold shifts of those blocks (wave-uniform)
+      int vc_any = 0;
+#pragma unroll
+      for (int jb = 0; jb < BPW; ++jb) vcs[jb] = 0;
       int slot = 0;  // ring stage of tile t
       for (int t = t_begin; t <= t_end; ++t) {
         const bool has_qk = t < t_end;
@@ -815,14 +894,19 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
         };
         // the copies of tile t+LEAD go out one share before each block's V
         half8_t vnh[BPW][2], vnl[BPW][2];
+        int vns[BPW];
+        int vn_any = 0;
 #pragma unroll
         for (int jb = 0; jb < BPW; ++jb) {
           if (has_qk) cp.issue_part(cdst, (t + LEAD) * 32, t + LEAD < t_end, jb, BPW);
+          vns[jb] = 0;
           if constexpr (KV16) read_v16<HD>(R::block(wave, jb), st, lane, vnh[jb]);
-          else convert_v<HD>(R::block(wave, jb), st, lane, vnh[jb], vnl[jb]);
+          else vns[jb] = convert_v<HD>(R::block(wave, jb), st, lane, vnh[jb], vnl[jb]);
+          vn_any |= vns[jb];
         }
         kconv();
         if (t > t_begin) {
+          if (vc_any) fold_scale(O, vcs, -1);
           const uint8_t* pf = pfrag[(t - 1) & 1];
           // vector tiles in groups of PG (registers)
           constexpr int PG = NQW * BPW > 6 ? 2 : NQW;
@@ -861,14 +945,18 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
                         hl == 1 ? vcl[jb][dd] : vch[jb][dd], hl == 2 ? pl[j] : ph[j], O[jb][i0 + j][dd], 0, 0, 0);
             }
           }
+          if (vc_any) fold_scale(O, vcs, 1);
         }
 #pragma unroll
-        for (int jb = 0; jb < BPW; ++jb)
+        for (int jb = 0; jb < BPW; ++jb) {
 #pragma unroll
           for (int dd = 0; dd < 2; ++dd) {
             vch[jb][dd] = vnh[jb][dd];
             if constexpr (!KV16) vcl[jb][dd] = vnl[jb][dd];
           }
+          vcs[jb] = vns[jb];
+        }
+        vc_any = vn_any;
         slot = (slot + 1 == D) ? 0 : slot + 1;
       }
       // copies into the ring past the last tile may still be landing

@@ -164,7 +164,8 @@ int verify_launch(const void* q, int q_dtype, const void* k, const uint16_t* k_s
   if (rows_per_group < 0 || n_splits < 0) return ATTNQ8_EINVAL;
   if (!(sm_scale >= 0.0f) || isinf(sm_scale)) return ATTNQ8_EINVAL;
   const int G = n_q_heads / n_kv_heads;
-  if (rows_per_group * G > kMaxVectorsPerGroup) return ATTNQ8_EINVAL;
+  // (the product in 64 bits: a huge rows_per_group must not wrap into range)
+  if ((long long)rows_per_group * G > kMaxVectorsPerGroup) return ATTNQ8_EINVAL;
   const int rg = rows_per_group > 0 ? rows_per_group : auto_rows_per_group(G, n_rows, head_dim);
   if (rg * G > max_vectors<KV16>(head_dim)) return ATTNQ8_EUNSUPPORTED;
   const int groups = (n_rows + rg - 1) / rg;
@@ -293,7 +294,7 @@ int attn_verify_q8_splits(int n_q_heads, int n_kv_heads, int head_dim, int ctx_l
   if (ctx_len < 0 || n_rows < 1 || n_rows > 32) return ATTNQ8_EINVAL;
   const int G = n_q_heads / n_kv_heads;
   if (G > kMaxVectorsPerGroup) return ATTNQ8_EUNSUPPORTED;
-  if (rows_per_group < 0 || rows_per_group * G > kMaxVectorsPerGroup) return ATTNQ8_EINVAL;
+  if (rows_per_group < 0 || (long long)rows_per_group * G > kMaxVectorsPerGroup) return ATTNQ8_EINVAL;
   const int rg = rows_per_group > 0 ? rows_per_group : auto_rows_per_group(G, n_rows, head_dim);
   const int groups = (n_rows + rg - 1) / rg;
   return splits_for(ctx_len + n_rows, groups * n_kv_heads, head_dim);

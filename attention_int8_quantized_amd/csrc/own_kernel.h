@@ -10,7 +10,8 @@
 // (no hand-off of p through LDS and no second barrier per tile).  The other
 // 8 - NQ waves feed them: they issue the direct-to-LDS copies of the int8 tiles
 // and, one tile ahead, convert K to fp16 fragments and V to exact fp16 hi + lo
-// fragments (dV * code) in LDS, where every compute wave reads them.  The
+// fragments (dV * code, with the general body's power-of-two shift for a block
+// holding a V scale above 512) in LDS, where every compute wave reads them.  The
 // arithmetic of each output element is the same as in the general attention
 // body (same q and p splits, same block order of the K scales, same three PV
 // terms in the same order, same reference-point policy), so the two produce
@@ -23,7 +24,8 @@
 //
 // LDS: a ring of three int8 stages (a stage is free once its tile has been
 // converted), double-buffered K fragments (16 KB), K scales (512 B) and V^T
-// fragments (32 KB): 151,552 B in all.  Over an fp16 cache nothing is
+// fragments (32 KB), and per tile a byte per block that carries the V fold's
+// shift (0 unless the block holds a V scale above 512): 151,568 B in all.  Over an fp16 cache nothing is
 // converted: the compute waves read K and V^T fragments from a ring of four
 // 32 KB stages, and the two feeders only copy.
 //
@@ -95,10 +97,13 @@ struct OwnFeeder {
     if constexpr (COPIES > 0) wait_vmcnt<COPIES * newer>();
   }
 
-  // Tile in stage `st` -> K fragments `kf`, K scales `ksd`, V^T fragments `vf`.
-  // Every read of the stage is issued before the first write, so the reads'
-  // latencies overlap.
-  __device__ __forceinline__ void convert(const uint8_t* st, uint8_t* kf, uint8_t* ksd, uint8_t* vf, int lane) const {
+  // Tile in stage `st` -> K fragments `kf`, K scales `ksd`, V^T fragments `vf`
+  // and the V fold shift of each of this feeder's blocks (one byte per block
+  // in `vsd`; 0 unless the block holds a V scale above 512).  Every read of
+  // the stage is issued before the first write, so the reads' latencies
+  // overlap.
+  __device__ __forceinline__ void convert(const uint8_t* st, uint8_t* kf, uint8_t* ksd, uint8_t* vf, uint8_t* vsd,
+                                          int lane) const {
     uint2 kw[NKU > 0 ? NKU : 1];
 #pragma unroll
     for (int j = 0; j < NKU; ++j) kw[j] = *(const uint2*)(st + k_rd[j]);
@@ -140,7 +145,8 @@ struct OwnFeeder {
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         scw[k] = __builtin_amdgcn_perm(srow[2 * k + 1][b >> 1], srow[2 * k][b >> 1], (b & 1) ? SEL1 : SEL0);
-      const half8_t sc = __builtin_bit_cast(half8_t, scw);
+      half8_t sc = __builtin_bit_cast(half8_t, scw);
+      const int sh = v_fold_prescale(sc);
 #pragma unroll
       for (int dd = 0; dd < 2; ++dd) {
         const half8_t c = codes8_to_f16((uint32_t)vw[j][dd][0], (uint32_t)vw[j][dd][1]);
@@ -150,6 +156,7 @@ struct OwnFeeder {
         *(half8_t*)(vf + ((d * 2 + 0) * 64 + lane) * 16) = vh8;
         *(half8_t*)(vf + ((d * 2 + 1) * 64 + lane) * 16) = vl8;
       }
+      if (lane == 0) vsd[b] = (uint8_t)sh;
     }
   }
 };
@@ -179,7 +186,8 @@ __device__ __forceinline__ void own_feed(const AttendArgs& a, size_t head_rows, 
       slot = slot + 1 == D ? 0 : slot + 1;
     }
     if (t + 1 < t_end)
-      fd.convert(r.ring + slot * L::BYTES, r.kfrag[(t + 1) & 1], r.kscale[(t + 1) & 1], r.vfrag[(t + 1) & 1], lane);
+      fd.convert(r.ring + slot * L::BYTES, r.kfrag[(t + 1) & 1], r.kscale[(t + 1) & 1], r.vfrag[(t + 1) & 1],
+                 r.vshift[(t + 1) & 1], lane);
   }
   wait_vmcnt<0>();  // copies past the last tile may still be landing
 }
@@ -236,12 +244,15 @@ __device__ __forceinline__ void attend_own_body(const AttendArgs& a) {
     uint8_t (*kfrag)[KF_BYTES];
     uint8_t (*vfrag)[VF_BYTES];
     uint8_t (*kscale)[KS_BYTES];
+    uint8_t (*vshift)[8];
   };
   __shared__ __attribute__((aligned(16))) uint8_t ring[D * L::BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t kfrag[2][KF_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t vfrag[2][VF_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t kscale[2][KS_BYTES];
-  Ring rg_{ring, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring, kfrag, vfrag, kscale};
+  __shared__ __attribute__((aligned(8))) uint8_t vshift[2][8];  // V fold shift per block (int8 cache)
+  Ring rg_{ring, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring, kfrag, vfrag, kscale,
+           vshift};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -518,6 +529,19 @@ __device__ __forceinline__ void attend_own_body(const AttendArgs& a) {
     } else {
     // O^T += (Vhi,Phi) + (Vlo,Phi) + (Vhi,Plo), four output tiles at a time
     const uint8_t* vf = vfrag[t & 1];
+    // a block with a shifted V fold (rare: a V scale above 512) takes this
+    // tile's sum in units of 2^s: O *= 2^-s before its MFMAs, O *= 2^s after
+    const uint2 shw = *(const uint2*)vshift[t & 1];
+    const bool shifted = (shw.x | shw.y) != 0;
+    auto fold_scale = [&](int sign) {
+#pragma unroll
+      for (int d = 0; d < NDT; ++d) {
+        const int b = d >> 1;
+        const int sh = ((b < 4 ? shw.x : shw.y) >> (8 * (b & 3))) & 0xff;
+        O[d] *= ldexpf(1.0f, sign * sh);
+      }
+    };
+    if (__builtin_expect(shifted, 0)) fold_scale(-1);
 #pragma unroll
     for (int d0 = 0; d0 < NDT; d0 += 4) {
       half8_t vh8[4], vl8[4];
@@ -533,6 +557,7 @@ __device__ __forceinline__ void attend_own_body(const AttendArgs& a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) O[d0 + i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vh8[i], plo, O[d0 + i], 0, 0, 0);
     }
+    if (__builtin_expect(shifted, 0)) fold_scale(1);
     }
   };
 

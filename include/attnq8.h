@@ -236,7 +236,10 @@ int attn_verify_head_greedy(const float* logits, int n_rows, int vocab,
  *
  * attnq8_status_string: a static description of a status code.
  * attnq8_last_path: a static per-thread description of the kernel variant,
- * grid and split count the calling thread's last successful call launched.
+ * grid and split count the calling thread's last successful call launched
+ * (the same idea as the expert kernels' report of which path ran: "Faster
+ * grouped and per-hit Q2_0 expert kernels, bitwise identical", What it does).
+ * Diagnostic only; it never changes which kernel runs.
  * ------------------------------------------------------------------------- */
 int attnq8_selftest_i8_to_f16(uint16_t* out, void* stream);
 #define ATTNQ8_STREAM_SINK_WORDS 1024

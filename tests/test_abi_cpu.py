@@ -52,6 +52,7 @@ def test_auto_splits(lib):
     assert f(4, 1, 96, 10, 4, 0) == _lib.EUNSUPPORTED
     assert f(4, 1, 64, 10, 33, 0) == _lib.EINVAL
     assert f(64, 1, 64, 10, 4, 4) == _lib.EINVAL  # 256 vectors per group > 128
+    assert f(8, 1, 64, 10, 4, 1 << 29) == _lib.EINVAL  # the product would wrap to 0 in 32 bits
 
 
 def _verify(lib, **kw):
@@ -80,6 +81,8 @@ def _verify(lib, **kw):
     (dict(ctx=297), _lib.EINVAL),          # ctx + rows > stride
     (dict(rg=-1), _lib.EINVAL),
     (dict(rg=40), _lib.EINVAL),            # 160 vectors per group
+    (dict(rg=1 << 29, hq=8, hkv=1), _lib.EINVAL),  # rows_per_group * G wraps to 0 in 32 bits
+    (dict(rg=(1 << 31) - 1), _lib.EINVAL),
     (dict(splits=10), _lib.EINVAL),        # more splits than 9 tiles
     (dict(splits=-2), _lib.EINVAL),
     (dict(sm=float("nan")), _lib.EINVAL),

@@ -124,3 +124,46 @@ def test_golden_files_name_their_source():
         with open(os.path.join(golden, name)) as f:
             head = f.read(2048)
         assert "source:" in head.lower(), f"tests/golden/{name} does not name its source"
+
+
+def test_prompt_f16kv_positions_and_brute_force():
+    """prompt_f16kv puts query i at q_pos0 + i: literal positions through the
+    pure-Python brute force on tiny fp16 caches (G in {1, 2, 3}, a chunk that
+    starts at key 0 and one that starts mid-cache)."""
+    import bruteforce
+
+    rng = np.random.default_rng(63)
+    for hq, hkv, hd, T, n, pos0, literal in ((4, 2, 32, 11, 3, 5, (5, 6, 7)),
+                                             (3, 1, 64, 9, 2, 0, (0, 1)),
+                                             (2, 2, 32, 6, 4, 2, (2, 3, 4, 5))):
+        k = rng.standard_normal((hkv, T, hd)).astype(np.float16)
+        v = (rng.standard_normal((hkv, T, hd)) * 3).astype(np.float16)
+        q = rng.standard_normal((n, hq, hd)).astype(np.float16)
+        got = oracle.prompt_f16kv(q, k, v, q_pos0=pos0)
+        ones = np.ones((hkv, T, hd // 32))
+        ref = np.array(bruteforce.attention(q, list(literal), k, ones, v, ones))
+        assert np.max(np.abs(got - ref)) <= 1e-12 * np.abs(ref).max()
+        with pytest.raises(TypeError):
+            oracle.prompt_f16kv(q, k, v.astype(np.float32), q_pos0=pos0)
+
+
+def test_prompt_f16kv_closed_forms():
+    """A query at position 0 sees only key 0 (output = V[0] exactly); keys
+    after a query's position never change it; a row subset equals the rows of
+    the whole chunk."""
+    rng = np.random.default_rng(64)
+    hkv, hq, hd, T = 1, 2, 64, 12
+    k = rng.standard_normal((hkv, T, hd)).astype(np.float16)
+    v = rng.standard_normal((hkv, T, hd)).astype(np.float16)
+    q = rng.standard_normal((4, hq, hd)).astype(np.float16)
+    out = oracle.prompt_f16kv(q, k, v, q_pos0=0)
+    for h in range(hq):
+        assert np.array_equal(out[0, h], v[0, 0].astype(np.float64))
+    k2, v2 = k.copy(), v.copy()
+    k2[:, 2:] = rng.standard_normal((hkv, T - 2, hd)).astype(np.float16)
+    v2[:, 2:] = rng.standard_normal((hkv, T - 2, hd)).astype(np.float16)
+    out2 = oracle.prompt_f16kv(q, k2, v2, q_pos0=0)
+    assert np.array_equal(out2[:2], out[:2])      # queries at 0 and 1 see keys 0..1 only
+    assert not np.array_equal(out2[2:], out[2:])  # the query at 2 sees key 2
+    sub = oracle.prompt_f16kv(q, k, v, q_pos0=0, rows=[1, 3])
+    assert np.array_equal(sub, out[[1, 3]])

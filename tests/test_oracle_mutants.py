@@ -137,3 +137,23 @@ def test_merge_pins_catch_mutant(name):
 def test_unmutated_oracle_passes_everything():
     assert _run_all_checks() == []
     assert math.isfinite(1.0)
+
+
+@pytest.mark.parametrize("shift", [-1, 1])
+def test_prompt_f16kv_position_mutants_fail(monkeypatch, shift):
+    """prompt_f16kv with its chunk placed one key early or late fails its pins."""
+    import test_oracle as T
+
+    def bad(q, k, v, q_pos0, sm_scale=None, rows=None):
+        n = np.asarray(q).shape[0]
+        return oa.attention_values(q, max(0, q_pos0 + shift) + np.arange(n), oa._fp16(k), oa._fp16(v),
+                                   sm_scale, rows)
+
+    monkeypatch.setattr(oracle, "prompt_f16kv", bad)
+    failed = 0
+    for pin in (T.test_prompt_f16kv_positions_and_brute_force, T.test_prompt_f16kv_closed_forms):
+        try:
+            pin()
+        except (AssertionError, IndexError, ValueError):
+            failed += 1
+    assert failed >= 1
