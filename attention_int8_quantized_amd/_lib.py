@@ -25,6 +25,8 @@ EHIP = -5
 F32 = 0
 F16 = 1
 
+STATIC_SCRATCH_BYTES = 32 << 20  # ATTNQ8_STATIC_SCRATCH_BYTES
+
 _c_int = ctypes.c_int
 _c_size = ctypes.c_size_t
 _c_float = ctypes.c_float
@@ -39,6 +41,11 @@ _SIGNATURES = {
          _c_int, _vp, _c_size, _c_float, _vp],
     ),
     "attn_reduce_partials": (_c_int, [_vp, _c_size, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
+    "attn_verify_q8_static": (
+        _c_int,
+        [_vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+         _c_int, _c_float, _vp, _vp],
+    ),
     "attn_prompt_q8": (
         _c_int,
         [_vp, _c_int, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,

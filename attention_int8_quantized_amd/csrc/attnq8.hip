@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+#include <mutex>
 #include <stdio.h>
 #include <string.h>
 
@@ -25,6 +26,41 @@ constexpr int kMaxAppendHeadDim = 4096;   // KV append: any multiple of 32 up to
 constexpr long long kAppendMaxBlocks = 8192;  // 32 workgroups per CU, then grid-stride
 
 thread_local char g_last_path[192] = "none";
+
+// The split partials of attn_verify_q8_static: one copy of this array on every
+// GPU the library runs on, held until the process ends.  In host code its
+// name stands for a host-side symbol, not a device address: kernels receive
+// the address scratch_address() obtained with hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[ATTNQ8_STATIC_SCRATCH_BYTES];
+
+// Device address of the current device's copy of `scratch`, looked up once per
+// device (with that device current) and kept; nullptr with *status set when
+// the runtime cannot provide it.
+void* scratch_address(int* status) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    *status = ATTNQ8_EHIP;
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *status = ATTNQ8_EUNSUPPORTED;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      *status = ATTNQ8_EHIP;
+      return nullptr;
+    }
+    addr[dev] = p;
+  }
+  *status = ATTNQ8_OK;
+  return addr[dev];
+}
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -151,11 +187,14 @@ int check_kv(const void* q, int q_dtype, const void* kc, const uint16_t* ks, con
 }
 
 // Verify launch for either cache format (KV16: fp16 K/V in k, v; no scales).
+// With dry set, only the host checks run (no HIP call, nothing launched) and
+// the workspace pointer is not examined.
 template <bool KV16>
 int verify_launch(const void* q, int q_dtype, const void* k, const uint16_t* k_scales, const void* v,
                   const uint16_t* v_scales, int n_q_heads, int n_kv_heads, int head_dim,
                   int kv_stride, int ctx_len, int n_rows, int rows_per_group, int n_splits,
-                  void* workspace, size_t workspace_bytes, float sm_scale, void* stream) {
+                  void* workspace, size_t workspace_bytes, float sm_scale, void* stream,
+                  bool dry = false) {
   int st = check_kv<KV16>(q, q_dtype, k, k_scales, v, v_scales, n_q_heads, n_kv_heads, head_dim,
                           kv_stride);
   if (st) return st;
@@ -173,10 +212,11 @@ int verify_launch(const void* q, int q_dtype, const void* k, const uint16_t* k_s
   const int tiles = (n_keys + 31) / 32;
   const int S = n_splits > 0 ? n_splits : splits_for(n_keys, groups * n_kv_heads, head_dim);
   if (S > tiles || S > 65535) return ATTNQ8_EINVAL;
-  if (!workspace) return ATTNQ8_EINVAL;
-  if (!aligned(workspace, 16)) return ATTNQ8_EALIGN;
+  if (!dry && !workspace) return ATTNQ8_EINVAL;
+  if (!dry && !aligned(workspace, 16)) return ATTNQ8_EALIGN;
   const size_t need = attn_verify_q8_workspace_bytes(n_rows, n_q_heads, head_dim, S);
   if (workspace_bytes < need) return ATTNQ8_EWORKSPACE;
+  if (dry) return ATTNQ8_OK;
 
   st = device_status();
   if (st) return st;
@@ -348,6 +388,43 @@ int attn_reduce_partials(const void* workspace, size_t workspace_bytes, int n_ro
   st = launch_status();
   if (st) return st;
   snprintf(g_last_path, sizeof(g_last_path), "reduce hd%d pairs%d splits%d", head_dim, pairs, n_splits);
+  return ATTNQ8_OK;
+}
+
+int attn_verify_q8_static(const void* q, int q_dtype, const int8_t* k_codes, const uint16_t* k_scales,
+                          const int8_t* v_codes, const uint16_t* v_scales, int n_q_heads, int n_kv_heads,
+                          int head_dim, int kv_stride, int ctx_len, int n_rows, int rows_per_group,
+                          int n_splits, float sm_scale, float* out, void* stream) {
+  // every check of both launches first, on the host
+  if (!out) return ATTNQ8_EINVAL;
+  if (!aligned(out, 16)) return ATTNQ8_EALIGN;
+  if (n_splits < 0) return ATTNQ8_EINVAL;
+  const int auto_splits =
+      attn_verify_q8_splits(n_q_heads, n_kv_heads, head_dim, ctx_len, n_rows, rows_per_group);
+  if (auto_splits < 0) return auto_splits;
+  const size_t per_split = attn_verify_q8_workspace_bytes(n_rows, n_q_heads, head_dim, 1);
+  const size_t fit = per_split ? (size_t)ATTNQ8_STATIC_SCRATCH_BYTES / per_split : 0;
+  if (fit < 1) return ATTNQ8_EWORKSPACE;
+  int S = n_splits;
+  if (S == 0) S = (size_t)auto_splits <= fit ? auto_splits : (int)fit;
+  else if ((size_t)S > fit) return ATTNQ8_EWORKSPACE;
+  int st = verify_launch<false>(q, q_dtype, k_codes, k_scales, v_codes, v_scales, n_q_heads, n_kv_heads,
+                                head_dim, kv_stride, ctx_len, n_rows, rows_per_group, S, nullptr,
+                                ATTNQ8_STATIC_SCRATCH_BYTES, sm_scale, stream, /*dry=*/true);
+  if (st) return st;
+  st = device_status();
+  if (st) return st;
+  void* ws = scratch_address(&st);
+  if (!ws) return st;
+  st = verify_launch<false>(q, q_dtype, k_codes, k_scales, v_codes, v_scales, n_q_heads, n_kv_heads,
+                            head_dim, kv_stride, ctx_len, n_rows, rows_per_group, S, ws,
+                            ATTNQ8_STATIC_SCRATCH_BYTES, sm_scale, stream);
+  if (st) return st;
+  char verify_path[sizeof(g_last_path)];
+  memcpy(verify_path, g_last_path, sizeof(verify_path));
+  st = attn_reduce_partials(ws, ATTNQ8_STATIC_SCRATCH_BYTES, n_rows, n_q_heads, head_dim, S, out, stream);
+  if (st) return st;
+  snprintf(g_last_path, sizeof(g_last_path), "static %.150s + reduce", verify_path);
   return ATTNQ8_OK;
 }
 

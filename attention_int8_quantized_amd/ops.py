@@ -121,6 +121,23 @@ def verify(q, k_codes, k_scales, v_codes, v_scales, ctx_len: int, rows_per_group
     return reduce_partials(ws, q.shape[0], q.shape[1], q.shape[2], S, out)
 
 
+def verify_static(q, k_codes, k_scales, v_codes, v_scales, ctx_len: int, out: torch.Tensor,
+                  rows_per_group: int = 0, n_splits: int = 0, sm_scale: float = 0.0) -> torch.Tensor:
+    """Verify attention through attn_verify_q8_static: the partials live in the
+    library's own scratch, so the call takes no workspace and allocates nothing;
+    the caller provides `out` [n_rows][Hq][hd] float32."""
+    n_rows, hq, hkv, hd, stride = _check_cache(q, k_codes, k_scales, v_codes, v_scales)
+    if out.dtype != torch.float32 or tuple(out.shape) != (n_rows, hq, hd) or not out.is_contiguous() \
+            or out.device != q.device:
+        raise ValueError("out must be a contiguous float32 tensor [n_rows][Hq][hd] on q's device")
+    st = _lib.load().attn_verify_q8_static(_ptr(q), _QTYPES[q.dtype], _ptr(k_codes), _ptr(k_scales),
+                                           _ptr(v_codes), _ptr(v_scales), hq, hkv, hd, stride, ctx_len,
+                                           n_rows, rows_per_group, n_splits, float(sm_scale), _ptr(out),
+                                           _stream())
+    _lib.check("attn_verify_q8_static", st)
+    return out
+
+
 def prompt(q, k_codes, k_scales, v_codes, v_scales, q_pos0: int, kv_len: Optional[int] = None,
            sm_scale: float = 0.0, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Causal prompt attention of q [n_queries][Hq][hd] at positions q_pos0 + i."""

@@ -29,8 +29,9 @@
  * fp16 scale.  head_dim is 64, 128 or 256.
  *
  * Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream),
- * never synchronise, never allocate device memory and keep no device state, so
- * they may be captured into a HIP graph.  Every argument check runs on the host
+ * never synchronise, never allocate device memory and keep no device state
+ * (except attn_verify_q8_static's scratch array, below), so they may be
+ * captured into a HIP graph.  Every argument check runs on the host
  * before anything is launched; on failure nothing is launched and a negative
  * status is returned.  A device fault surfaces at the caller's next
  * synchronisation, as for any HIP launch.  There is one code path per call: no
@@ -111,6 +112,37 @@ int attn_verify_q8(const void* q, int q_dtype,
 int attn_reduce_partials(const void* workspace, size_t workspace_bytes,
                          int n_rows, int n_q_heads, int head_dim, int n_splits,
                          float* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * attn_verify_q8_static: for callers that cannot allocate device memory --
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc -- and so cannot provide attn_verify_q8's workspace.  It runs
+ * attn_verify_q8 and then attn_reduce_partials on `stream` with the split
+ * partials in a scratch array the library keeps in device memory
+ * (ATTNQ8_STATIC_SCRATCH_BYTES on every GPU it runs on, held until the process
+ * ends), and writes the normalised fp32 output to `out`
+ * [n_rows][n_q_heads][head_dim] (16-byte aligned).  It calls no allocator.
+ *
+ * Arguments and requirements as attn_verify_q8; n_splits = 0 takes
+ * attn_verify_q8_splits() capped to what the scratch holds
+ * (ATTNQ8_STATIC_SCRATCH_BYTES / attn_verify_q8_workspace_bytes(n_rows,
+ * n_q_heads, head_dim, 1) splits); an explicit n_splits beyond that, or a
+ * shape of which not even one split fits, returns ATTNQ8_EWORKSPACE with
+ * nothing launched.  With the same split count the output is bitwise the
+ * output of attn_verify_q8 followed by attn_reduce_partials.
+ *
+ * Every call on one GPU uses that GPU's single scratch array: calls that
+ * overlap on one GPU (on different streams or host threads without ordering)
+ * race and may return wrong results.  Calls ordered on one stream are safe.
+ * ------------------------------------------------------------------------- */
+#define ATTNQ8_STATIC_SCRATCH_BYTES (32u << 20)
+int attn_verify_q8_static(const void* q, int q_dtype,
+                          const int8_t* k_codes, const uint16_t* k_scales,
+                          const int8_t* v_codes, const uint16_t* v_scales,
+                          int n_q_heads, int n_kv_heads, int head_dim,
+                          int kv_stride, int ctx_len, int n_rows,
+                          int rows_per_group, int n_splits,
+                          float sm_scale, float* out, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Prompt attention ("hip: gfx12 (RDNA4) WMMA kernel for the int8-KV QSA prompt

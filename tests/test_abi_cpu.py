@@ -225,3 +225,34 @@ def test_selftest_rejects_null(lib):
 def test_library_is_in_tree():
     assert os.path.dirname(_lib.LIB_PATH).endswith("attention_int8_quantized_amd")
     assert isinstance(_lib.load(), ctypes.CDLL)
+
+
+def _static(lib, **kw):
+    args = dict(q=A, q_dtype=0, kc=A, ks=A, vc=A, vs=A, hq=4, hkv=1, hd=64, stride=300, ctx=256,
+                rows=4, rg=0, splits=0, sm=0.0, out=A, stream=None)
+    args.update(kw)
+    return lib.attn_verify_q8_static(args["q"], args["q_dtype"], args["kc"], args["ks"], args["vc"],
+                                     args["vs"], args["hq"], args["hkv"], args["hd"], args["stride"],
+                                     args["ctx"], args["rows"], args["rg"], args["splits"], args["sm"],
+                                     args["out"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=None), _lib.EINVAL),
+    (dict(out=A + 4), _lib.EALIGN),
+    (dict(q=None), _lib.EINVAL),
+    (dict(kc=A + 4), _lib.EALIGN),
+    (dict(hd=96), _lib.EUNSUPPORTED),
+    (dict(rows=33), _lib.EINVAL),
+    (dict(splits=-1), _lib.EINVAL),
+    (dict(splits=10), _lib.EINVAL),                 # more splits than 9 tiles
+    (dict(rg=1 << 29, hq=8), _lib.EINVAL),
+    # one row of 128 heads at head_dim 256 holds 132,096 B of partials per split:
+    # 254 splits fit the scratch, 255 do not
+    (dict(hq=128, hd=256, stride=20000, ctx=16384, rows=1, splits=255), _lib.EWORKSPACE),
+    # 32 rows of 1,024 heads: not even one split fits
+    (dict(hq=1024, hkv=8, hd=256, stride=20000, ctx=16384, rows=32, splits=1), _lib.EWORKSPACE),
+    (dict(hq=1024, hkv=8, hd=256, stride=20000, ctx=16384, rows=32, splits=0), _lib.EWORKSPACE),
+])
+def test_static_verify_rejects_before_any_hip_call(lib, kw, status):
+    assert _static(lib, **kw) == status
