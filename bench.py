@@ -1,18 +1,25 @@
 """Benchmark of the int8-KV attention hot path on one MI355X.
 
 One step = one verify call (attn_verify_q8 + attn_reduce_partials) on the
-verify-window workload (24 Q / 4 KV heads, head_dim 256, context 20,676, 8
-sequential rows) followed by one prompt call (attn_prompt_q8) on the prompt
-chunk (12 Q / 1 KV head, head_dim 256, 32,768-token int8 context, 2,048 causal
-queries).  Inputs are seeded synthetic data resident in HBM before timing, in
-several rotating copies so that the 256 MB Infinity Cache cannot serve
-repeats.  Durations come from HIP events recorded on the library's stream:
-around each whole verify call (attention kernel + reducer, nothing recorded
-between them) and each prompt call, and on alternate steps one more event after
-the attention kernel, which times it alone for its roofline.  The GPU is held by
-a spin kernel while the timed launches are queued so that host submission
-latency does not enter them.  The practical HBM read ceiling (a plain 1 GiB
-read by the library's attnq8_stream_read) is reported beside the 8 TB/s peak.
+long-context verify workload (24 Q / 4 KV heads, head_dim 256, context 131,072,
+4 sequential rows, 1% of K positions x8) followed by one prompt call
+(attn_prompt_q8) on the prompt chunk (12 Q / 1 KV head, head_dim 256,
+32,768-token int8 context, 2,048 causal queries).  The headline `value` is the
+verify call's KV GB/s; the prompt's TFLOP/s is reported beside it.  The other
+verify configurations (the verify window, the verify batch with the pages' R4
+row groups and with the library's own grouping, the tiny verify) are timed in
+the same run and reported in `verify_configs`.
+
+Inputs are seeded synthetic data resident in HBM before timing, each workload
+in rotating copies of at least 1 GB (four times the 256 MB Infinity Cache)
+so that repeats come from HBM.  Durations come from HIP events recorded on the
+library's stream: around each whole verify call (attention kernel + reducer,
+nothing recorded between them) and each prompt call, and on alternate steps one
+more event after the attention kernel, which times it alone for its roofline.
+The GPU is held by a spin kernel while the timed launches are queued so that
+host submission latency does not enter them.  The practical HBM read ceiling
+(a plain 1 GiB read by the library's attnq8_stream_read) is reported beside the
+8 TB/s peak.
 
 Prints one JSON line.  Other modes:
   --copy-calibration   run only plain device copies of a known size (for
@@ -26,6 +33,10 @@ Prints one JSON line.  Other modes:
   --oracle-times       the fp64 oracle per workload on the host (bounded
                        samples, no GPU) and the tests' pure-Python brute force
                        on the tiny verify; one JSON line per workload
+  --summarize-trace F  per-kernel durations from a rocprofv3 kernel-trace CSV,
+                       grouped by kernel and grid, the first --skip-first
+                       launches of each group (the warm-up) left out; a
+                       markdown table (no GPU)
 """
 
 from __future__ import annotations
@@ -54,8 +65,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--verify-workload", default="verify_window")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--verify-workload", default="long_verify")
     ap.add_argument("--prompt-workload", default="prompt_chunk")
     ap.add_argument("--no-prompt", action="store_true")
     ap.add_argument("--no-append", action="store_true")
@@ -67,6 +78,12 @@ def parse():
     ap.add_argument("--sweep", action="store_true")
     ap.add_argument("--oracle-times", action="store_true",
                     help="time the fp64 oracle per workload on the host (no GPU)")
+    ap.add_argument("--no-extra-verify", action="store_true",
+                    help="skip the other verify configurations")
+    ap.add_argument("--summarize-trace", default=None,
+                    help="a rocprofv3 *_kernel_trace.csv to summarise (no GPU)")
+    ap.add_argument("--skip-first", type=int, default=6,
+                    help="launches per (kernel, grid) group left out by --summarize-trace")
     return ap.parse_args()
 
 
@@ -124,6 +141,9 @@ def main():
     if args.oracle_times:
         oracle_times()
         return
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.skip_first)
+        return
 
     import torch
 
@@ -138,11 +158,8 @@ def main():
     # ---------------- inputs (host -> device, then device-side copies) ----------
     log(f"generating {wv.name}")
     iv = W.generate(wv)
-    v_host = [iv.q, iv.k_codes, iv.k_scales, iv.v_codes, iv.v_scales]
-    kv_bytes_v = sum(x.nbytes for x in v_host[1:])
-    nv = max(1, min(64, int(args.rotate_bytes // max(kv_bytes_v, 1)) + 1))
-    base = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in v_host]
-    vbufs = [base] + [[t.clone() for t in base] for _ in range(nv - 1)]
+    vbufs = rotating_copies([iv.q, iv.k_codes, iv.k_scales, iv.v_codes, iv.v_scales], dev,
+                            args.rotate_bytes)
     S = args.splits or ops.verify_splits(wv.n_q_heads, wv.n_kv_heads, wv.head_dim, wv.ctx_len,
                                          wv.n_rows, args.rows_per_group)
     ws = torch.empty(ops.workspace_bytes(wv.n_rows, wv.n_q_heads, wv.head_dim, S), dtype=torch.uint8,
@@ -153,11 +170,8 @@ def main():
     if not args.no_prompt:
         log(f"generating {wp.name}")
         ip = W.generate(wp)
-        p_host = [ip.q, ip.k_codes, ip.k_scales, ip.v_codes, ip.v_scales]
-        pbytes = sum(x.nbytes for x in p_host)
-        npb = max(1, min(16, int(0.35e9 // pbytes) + 1))
-        pbase = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in p_host]
-        pbufs = [pbase] + [[t.clone() for t in pbase] for _ in range(npb - 1)]
+        pbufs = rotating_copies([ip.q, ip.k_codes, ip.k_scales, ip.v_codes, ip.v_scales], dev,
+                                args.rotate_bytes)
         pout = torch.empty((wp.n_queries, wp.n_q_heads, wp.head_dim), dtype=torch.float32,
                            device=dev)
     torch.cuda.synchronize()
@@ -174,29 +188,31 @@ def main():
         q, kc, ks, vc, vs = pbufs[i % len(pbufs)]
         ops.prompt(q, kc, ks, vc, vs, q_pos0=wp.pos0, kv_len=wp.kv_len, out=pout)
 
-    # ---------------- warmup -----------------------------------------------------
-    for i in range(args.warmup):
-        verify_call(i)
-        reduce_call()
-        if pbufs:
-            prompt_call(i)
-    torch.cuda.synchronize()
     verify_call(0)
     verify_path = ops.last_path()
     prompt_path = None
     if pbufs:
         prompt_call(0)
         prompt_path = ops.last_path()
-    torch.cuda.synchronize()
+    hold = Hold(ops, dev)
 
-    # ---------------- timed region ------------------------------------------------
+    # ---------------- warmup, then the timed region --------------------------------
+    # The warm-up steps run back to back, so that the clocks have settled when
+    # timing starts (after an idle gap the first launches run up to 25% slower);
+    # a short busy hold keeps the GPU working while the first timed launches are
+    # queued.
     K = args.steps
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     ev = [[E() for _ in range(4)] for _ in range(K)]
     t_start, t_end = E(), E()
     torch.cuda.synchronize()
-    # hold the GPU while the launches are queued (~50 us of host time per step)
-    torch.cuda._sleep(int(2.4e9 * (0.06e-3 * K + 0.02)))
+    for i in range(args.warmup):
+        verify_call(i)
+        reduce_call()
+        if pbufs:
+            prompt_call(i)
+    torch.cuda.synchronize()
+    hold(1e-3)
     wall0 = time.perf_counter()
     t_start.record()
     # Events bracket the verify call (kernel + reducer) and the prompt call of
@@ -226,14 +242,12 @@ def main():
     step_ms = t_start.elapsed_time(t_end) / K
 
     # KV bytes of the grouping the library used (rows_per_group 0 = its choice)
-    m = re.search(r"rows_per_group(\d+)", verify_path or "")
-    rg_used = int(m.group(1)) if m else (args.rows_per_group or wv.rows_per_group)
+    rg_used = rows_per_group_of(verify_path, args.rows_per_group or wv.rows_per_group)
     vbytes = wv.visible_kv_bytes(rg_used)
     verify_s = float(np.mean(kv))
     gbs = vbytes / verify_s / 1e9
     k1_mean = float(np.mean(k1))
     k1_gbs = vbytes / k1_mean / 1e9
-    tr_v = load_traffic("verify")
 
     res = {
         "metric": METRIC,
@@ -252,6 +266,7 @@ def main():
             "workload": wv.name,
             "verify": {**W.describe(wv), "rows_per_group": rg_used, "splits": S,
                        "rotating_copies": len(vbufs), "path": verify_path},
+            "prompt_workload": wp.name if pbufs else None,
             "parallelism": "single-gpu",
         },
         "verify": {
@@ -260,39 +275,49 @@ def main():
             "reduce_us": round((verify_s - k1_mean) * 1e6, 3),
             "kv_bytes": vbytes,
             "unique_kv_bytes": wv.unique_kv_bytes(),
+            "partial_bytes": ops.workspace_bytes(wv.n_rows, wv.n_q_heads, wv.head_dim, S),
             "gbs": round(gbs, 2),
             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "kernel_gbs": round(k1_gbs, 2),
+            "kernel_frac_hbm": round(k1_gbs / HBM_PEAK_GBS, 4),
         },
         "roofline": {
-            "kernel": "attend_q8_kernel (verify)",
+            "kernel": kernel_of_path(verify_path),
             "bound": "hbm",
             "achieved": round(k1_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
-            "traffic": tr_v,
+            "traffic": load_traffic("verify"),
         },
     }
     if pbufs:
         flops = wp.algorithmic_flops()
+        issued = issued_mfma_flops(wp, prompt_path)
         kp_mean = float(np.mean(kp))
         tf = flops / kp_mean / 1e12
+        tfi = issued / kp_mean / 1e12
         res["prompt"] = {
             "workload": wp.name,
             "config": W.describe(wp),
             "path": prompt_path,
             "ms_per_call": round(kp_mean * 1e3, 4),
+            "algorithmic_flop": flops,
+            "issued_mfma_flop": issued,
             "tflops": round(tf, 2),
             "frac_mfma": round(tf / FP16_MFMA_PEAK_TFLOPS, 4),
+            "issued_tflops": round(tfi, 2),
+            "frac_mfma_issued": round(tfi / FP16_MFMA_PEAK_TFLOPS, 4),
             "rotating_copies": len(pbufs),
         }
         res["prompt_roofline"] = {
-            "kernel": "attend_own_q8_kernel (prompt)",
+            "kernel": kernel_of_path(prompt_path),
             "bound": "mfma",
             "achieved": round(tf, 2),
             "peak": FP16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(tf / FP16_MFMA_PEAK_TFLOPS, 4),
+            "frac_issued": round(tfi / FP16_MFMA_PEAK_TFLOPS, 4),
             "traffic": load_traffic("prompt"),
         }
     res["host_wall_s"] = round(wall, 3)
@@ -300,15 +325,195 @@ def main():
     res["read_ceiling"] = ceil
     res["verify"]["frac_of_read_ceiling"] = round(gbs / ceil["gbs"], 4)
     res["verify"]["kernel_frac_of_read_ceiling"] = round(k1_gbs / ceil["gbs"], 4)
+    if not args.no_extra_verify:
+        res["verify_configs"] = time_verify_configs(ops, dev, args, min(K, 30), hold)
     if not args.no_append:
-        res["kv_append"] = time_append(ops, dev, min(K, 20), args.warmup)
-        res["verify_head"] = time_head(ops, dev, min(K, 20), args.warmup)
-        res.update(time_f16kv(ops, dev, wv, wp, min(K, 20), args.warmup, not args.no_prompt))
+        res["kv_append"] = time_append(ops, dev, min(K, 20), args.warmup, hold)
+        res["verify_head"] = time_head(ops, dev, min(K, 20), args.warmup, hold)
+        res.update(time_f16kv(ops, dev, wv, wp, min(K, 20), args.warmup, not args.no_prompt, hold))
 
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(wv, iv)
 
     print(json.dumps(res), flush=True)
+
+
+class Hold:
+    """Keeps the GPU busy while launches are being queued: plain reads of a
+    1 GiB buffer (about 0.17 ms each on this part), so that the timed launches
+    find the queue ahead of them without the clocks dropping as they would
+    behind an idle wait."""
+
+    def __init__(self, ops, dev, nbytes=1 << 30):
+        import torch
+
+        self.ops = ops
+        self.buf = torch.zeros(nbytes // 4, dtype=torch.int32, device=dev)
+        self.sink = torch.empty(ops.STREAM_SINK_WORDS, dtype=torch.int32, device=dev)
+
+    def __call__(self, seconds):
+        for _ in range(max(1, int(seconds / 0.15e-3) + 1)):
+            self.ops.stream_read(self.buf, self.sink)
+
+
+def timed_calls(call, steps, warmup, hold, per_call_host_s=60e-6, marks=2):
+    """Warm-up calls back to back, then `steps` timed calls, all queued behind a
+    busy hold long enough for the host to queue them; returns the events
+    (marks per call) after synchronising.  call(i, events) records its own
+    events."""
+    import torch
+
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    ev = [[E() for _ in range(marks)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    hold(per_call_host_s * (warmup + steps) + 1e-3)
+    for i in range(warmup):
+        call(i, None)
+    for i in range(steps):
+        call(i + 1, ev[i])
+    torch.cuda.synchronize()
+    return ev
+
+
+def rotating_copies(host_arrays, dev, min_bytes, cap=512):
+    """Device copies of one workload's inputs, enough of them that at least
+    min_bytes cycle (each copy holds every input array)."""
+    import torch
+
+    per = sum(a.nbytes for a in host_arrays)
+    n = max(1, min(cap, -(-int(min_bytes) // max(per, 1))))
+    base = [torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in host_arrays]
+    return [base] + [[t.clone() for t in base] for _ in range(n - 1)]
+
+
+def rows_per_group_of(path, default):
+    m = re.search(r"rows_per_group(\d+)", path or "")
+    return int(m.group(1)) if m else default
+
+
+def kernel_of_path(path):
+    """The attention kernel instance a launch description names."""
+    if not path:
+        return None
+    kv16 = "kvf16" in path
+    hd = re.search(r"hd(\d+)", path).group(1)
+    qf32 = "qf32" in path
+    nq = re.search(r"tiles(\d+)", path).group(1)
+    final = path.startswith("prompt")
+    b = lambda x: "true" if x else "false"  # noqa: E731
+    if " own" in path:
+        name = "attend_own_f16kv_kernel" if kv16 else "attend_own_q8_kernel"
+        return f"{name}<{b(qf32)}, {b(final)}, {nq}>"
+    name = "attend_f16kv_kernel" if kv16 else "attend_q8_kernel"
+    return f"{name}<{hd}, {b(qf32)}, {b(final)}, {nq}>"
+
+
+def issued_mfma_flops(w, path):
+    """FLOPs of the 16x16x32 f16 MFMAs (16,384 each) the attention kernel issues
+    for workload w in the launch `path` describes: per (16-vector tile, 32-key
+    tile) QK takes head_dim/32 blocks x 2 key subtiles (x2 for fp32 q: hi and
+    lo), PV head_dim/16 output tiles x 3 terms (Vhi Phi, Vlo Phi, Vhi Plo; two
+    over an fp16 cache).  Each row group scans keys 0 .. its last row's
+    position, in whole 32-key tiles."""
+    hd = w.head_dim
+    qf32 = "qf32" in path
+    kv16 = "kvf16" in path
+    rg = rows_per_group_of(path, 1)
+    per_pair = (hd // 32) * 2 * (2 if qf32 else 1) + (hd // 16) * (2 if kv16 else 3)
+    if w.kind == "prompt":
+        n, p0 = w.n_queries, w.pos0
+    else:
+        n, p0 = w.n_rows, w.ctx_len
+    total = 0
+    for r0 in range(0, n, rg):
+        nr = min(rg, n - r0)
+        vtiles = -(-nr * w.group // 16)
+        ktiles = -(-(p0 + r0 + nr) // 32)
+        total += vtiles * ktiles
+    return total * w.n_kv_heads * per_pair * 16384
+
+
+# The verify configurations reported beside the headline: (workload, rows_per_group,
+# label); rows_per_group 0 = the library's own grouping.
+EXTRA_VERIFY = [("verify_window", 0, "verify_window"), ("verify_batch", 4, "verify_batch_r4"),
+                ("verify_batch", 0, "verify_batch_auto"), ("tiny_verify", 0, "tiny_verify")]
+
+
+def time_verify_configs(ops, dev, args, steps, hold):
+    """The other verify workloads: whole call and attention kernel alone (HIP
+    events, rotating copies of >= rotate_bytes), KV bytes per pass over the row
+    groups and unique, and the partials' bytes."""
+    import torch
+
+    import workloads as W
+
+    out = {}
+    cache = {}
+    for name, rg, label in EXTRA_VERIFY:
+        w = W.WORKLOADS[name]
+        if name not in cache:
+            cache.clear()
+            torch.cuda.empty_cache()
+            inp = W.generate(w)
+            cache[name] = rotating_copies([inp.q, inp.k_codes, inp.k_scales, inp.v_codes, inp.v_scales],
+                                          dev, args.rotate_bytes)
+        bufs = cache[name]
+        k1, k2, S, path = time_verify(ops, bufs, w, rg, steps, args.warmup, hold)
+        rg_used = rows_per_group_of(path, rg or w.rows_per_group)
+        per_pass = w.visible_kv_bytes(rg_used)
+        uniq = w.unique_kv_bytes()
+        tot = k1 + k2
+        out[label] = {
+            "workload": name,
+            "rows_per_group": rg_used,
+            "splits": S,
+            "path": path,
+            "kernel": kernel_of_path(path),
+            "us_per_call": round(tot * 1e6, 3),
+            "kernel_us": round(k1 * 1e6, 3),
+            "reduce_us": round(k2 * 1e6, 3),
+            "kv_bytes_per_pass": per_pass,
+            "unique_kv_bytes": uniq,
+            "partial_bytes": ops.workspace_bytes(w.n_rows, w.n_q_heads, w.head_dim, S),
+            "gbs_per_pass": round(per_pass / tot / 1e9, 2),
+            "gbs_unique": round(uniq / tot / 1e9, 2),
+            "frac_hbm_per_pass": round(per_pass / tot / 1e9 / HBM_PEAK_GBS, 4),
+            "kernel_gbs_per_pass": round(per_pass / k1 / 1e9, 2),
+            "kernel_frac_hbm_per_pass": round(per_pass / k1 / 1e9 / HBM_PEAK_GBS, 4),
+            "rotating_copies": len(bufs),
+            "steps": steps,
+        }
+    cache.clear()
+    torch.cuda.empty_cache()
+    return out
+
+
+def summarize_trace(path, skip_first):
+    """Per-kernel durations from a rocprofv3 kernel-trace CSV: launches grouped by
+    (kernel, grid), the first skip_first of each group dropped; markdown table."""
+    import csv
+    import statistics
+
+    groups = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            if row.get("Kind") != "KERNEL_DISPATCH":
+                continue
+            key = (row["Kernel_Name"], (row["Grid_Size_X"], row["Grid_Size_Y"], row["Grid_Size_Z"]),
+                   row["Workgroup_Size_X"])
+            dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) * 1e-3  # us
+            groups.setdefault(key, []).append((int(row["Dispatch_Id"]), dur))
+    print(f"| kernel | grid (threads) | block | launches used (of all) | median (us) | mean (us) | min (us) | max (us) |")
+    print("|---|---|---|---|---|---|---|---|")
+    rows = []
+    for (name, grid, block), d in groups.items():
+        d.sort()
+        used = [x for _, x in d[skip_first:]] or [x for _, x in d]
+        rows.append((statistics.median(used) * len(used), name, grid, block, used, len(d)))
+    for _, name, grid, block, used, n_all in sorted(rows, reverse=True):
+        short = name if len(name) <= 110 else name[:107] + "..."
+        print(f"| `{short}` | {'x'.join(grid)} | {block} | {len(used)} ({n_all}) | "
+              f"{statistics.median(used):.2f} | {statistics.mean(used):.2f} | {min(used):.2f} | {max(used):.2f} |")
 
 
 def read_ceiling(ops, dev, nbytes=1 << 30, reps=10):
@@ -440,7 +645,7 @@ def cpu_baseline(wv, iv):
 APPEND_SHAPE = (32768, 4, 256)
 
 
-def time_append(ops, dev, steps, warmup):
+def time_append(ops, dev, steps, warmup, hold):
     import torch
 
     T, H, hd = APPEND_SHAPE
@@ -452,23 +657,17 @@ def time_append(ops, dev, steps, warmup):
     ks = torch.empty((H, T, hd // 32), dtype=torch.float16, device=dev)
     vs = torch.empty_like(ks)
 
-    def call(i):
+    def call(i, e):
         k, v = rows[i % 2]
+        if e:
+            e[0].record()
         ops.kv_append(k, kc, ks, 0, v, vc, vs)
+        if e:
+            e[1].record()
 
-    for i in range(warmup):
-        call(i)
-    call(0)
+    call(0, None)
     path = ops.last_path()
-    torch.cuda.synchronize()
-    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    ev = [(E(), E()) for _ in range(steps)]
-    torch.cuda._sleep(int(2.4e9 * (0.05e-3 * steps + 0.02)))
-    for i in range(steps):
-        ev[i][0].record()
-        call(i + 1)
-        ev[i][1].record()
-    torch.cuda.synchronize()
+    ev = timed_calls(call, steps, warmup, hold)
     t = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
     n = T * H * hd
     moved = 2 * (n * 4 + n + (n // 32) * 2)  # K and V: fp32 rows read, codes + scales written
@@ -485,24 +684,21 @@ def time_append(ops, dev, steps, warmup):
     }
 
 
-def _events_mean(call, steps, warmup):
-    import torch
+def _events_mean(call, steps, warmup, hold):
+    """Mean duration (s) of call(i) over `steps` timed calls (timed_calls)."""
 
-    for i in range(warmup):
+    def c(i, e):
+        if e:
+            e[0].record()
         call(i)
-    torch.cuda.synchronize()
-    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    ev = [(E(), E()) for _ in range(steps)]
-    torch.cuda._sleep(int(2.4e9 * (0.05e-3 * steps + 0.02)))
-    for i in range(steps):
-        ev[i][0].record()
-        call(i + 1)
-        ev[i][1].record()
-    torch.cuda.synchronize()
+        if e:
+            e[1].record()
+
+    ev = timed_calls(c, steps, warmup, hold)
     return float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
 
 
-def time_f16kv(ops, dev, wv, wp, steps, warmup, with_prompt):
+def time_f16kv(ops, dev, wv, wp, steps, warmup, with_prompt, hold):
     """The verify and prompt workloads over an fp16 K/V cache (the same seeded
     draws rounded to fp16 instead of quantised), measured beside the int8 path."""
     import torch
@@ -511,9 +707,7 @@ def time_f16kv(ops, dev, wv, wp, steps, warmup, with_prompt):
 
     out = {}
     iv = W.generate_f16kv(wv)
-    base = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (iv.q, iv.k, iv.v)]
-    kvb = base[1].numel() * 2 + base[2].numel() * 2
-    copies = [base] + [[t.clone() for t in base] for _ in range(max(0, int(1.1e9 // kvb)))]
+    copies = rotating_copies([iv.q, iv.k, iv.v], dev, 1.1e9)
     S = ops.verify_splits(wv.n_q_heads, wv.n_kv_heads, wv.head_dim, wv.ctx_len, wv.n_rows, 0)
     ws = torch.empty(ops.workspace_bytes(wv.n_rows, wv.n_q_heads, wv.head_dim, S),
                      dtype=torch.uint8, device=dev)
@@ -525,10 +719,9 @@ def time_f16kv(ops, dev, wv, wp, steps, warmup, with_prompt):
 
     vcall(0)
     vpath = ops.last_path()
-    t = _events_mean(vcall, steps, warmup)
+    t = _events_mean(vcall, steps, warmup, hold)
     # fp16 K and V bytes of the grouping the library chose
-    m = re.search(r"rows_per_group(\d+)", vpath or "")
-    rg = int(m.group(1)) if m else wv.rows_per_group
+    rg = rows_per_group_of(vpath, wv.rows_per_group)
     vis = wv.visible_kv_bytes(rg) // (2 * (wv.head_dim + wv.head_dim // 16)) * 4 * wv.head_dim
     out["verify_f16kv"] = {
         "workload": f"{wv.name} over an fp16 cache",
@@ -541,13 +734,13 @@ def time_f16kv(ops, dev, wv, wp, steps, warmup, with_prompt):
         "traffic": load_traffic("verify_f16kv"),
     }
     ops.reduce_partials(ws, wv.n_rows, wv.n_q_heads, wv.head_dim, S, out=o)
-    del copies, base
+    del copies
+    torch.cuda.empty_cache()
     if with_prompt:
         ip = W.generate_f16kv(wp)
-        pb = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (ip.q, ip.k, ip.v)]
         pout = torch.empty((wp.n_queries, wp.n_q_heads, wp.head_dim), dtype=torch.float32,
                            device=dev)
-        pcopies = [pb] + [[t.clone() for t in pb] for _ in range(7)]
+        pcopies = rotating_copies([ip.q, ip.k, ip.v], dev, 1.1e9)
 
         def pcall(i):
             q, k, v = pcopies[i % len(pcopies)]
@@ -555,14 +748,16 @@ def time_f16kv(ops, dev, wv, wp, steps, warmup, with_prompt):
 
         pcall(0)
         ppath = ops.last_path()
-        tp = _events_mean(pcall, max(3, steps // 4), 1)
+        tp = _events_mean(pcall, max(3, steps // 4), max(3, warmup // 4), hold)
         tf = wp.algorithmic_flops() / tp / 1e12
+        tfi = issued_mfma_flops(wp, ppath) / tp / 1e12
         out["prompt_f16kv"] = {
             "workload": f"{wp.name} over an fp16 cache",
             "path": ppath,
             "ms_per_call": round(tp * 1e3, 4),
             "tflops": round(tf, 2),
             "frac_mfma": round(tf / FP16_MFMA_PEAK_TFLOPS, 4),
+            "frac_mfma_issued": round(tfi / FP16_MFMA_PEAK_TFLOPS, 4),
             "traffic": load_traffic("prompt_f16kv"),
         }
     return out
@@ -574,7 +769,7 @@ def time_f16kv(ops, dev, wv, wp, steps, warmup, with_prompt):
 HEAD_SHAPE = (5, 248320)
 
 
-def time_head(ops, dev, steps, warmup):
+def time_head(ops, dev, steps, warmup, hold):
     import torch
 
     rows, V = HEAD_SHAPE
@@ -585,22 +780,16 @@ def time_head(ops, dev, steps, warmup):
     tok = torch.empty(rows, dtype=torch.int32, device=dev)
     top = torch.empty(rows, dtype=torch.float32, device=dev)
 
-    def call(i):
+    def call(i, e):
+        if e:
+            e[0].record()
         ops.verify_head_greedy(copies[i % len(copies)], workspace=ws, token=tok, top_prob=top)
+        if e:
+            e[1].record()
 
-    for i in range(warmup):
-        call(i)
-    call(0)
+    call(0, None)
     path = ops.last_path()
-    torch.cuda.synchronize()
-    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    ev = [(E(), E()) for _ in range(steps)]
-    torch.cuda._sleep(int(2.4e9 * (0.05e-3 * steps + 0.02)))
-    for i in range(steps):
-        ev[i][0].record()
-        call(i + 1)
-        ev[i][1].record()
-    torch.cuda.synchronize()
+    ev = timed_calls(call, steps, warmup, hold)
     t = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
     moved = rows * V * 4
     return {
@@ -624,7 +813,7 @@ SWEEP_ROWS = 8
 SWEEP_GROUPS = (1, 4, 8)
 
 
-def time_verify(ops, bufs, w, rows_per_group, steps, warmup):
+def time_verify(ops, bufs, w, rows_per_group, steps, warmup, hold):
     """Mean durations (s) over rotating inputs: the attention kernel alone, and the
     rest of the verify call (reducer and the launch gap before it)."""
     import torch
@@ -636,32 +825,26 @@ def time_verify(ops, bufs, w, rows_per_group, steps, warmup):
     out = torch.empty((w.n_rows, w.n_q_heads, w.head_dim), dtype=torch.float32,
                       device=ws.device)
 
-    def call(i):
+    paths = []
+
+    # (as in the main run: the kernel alone on odd steps, the whole call on even ones)
+    def call(i, e):
         q, kc, ks, vc, vs = bufs[i % len(bufs)]
+        if e:
+            e[0].record()
         ops.verify_partials(q, kc, ks, vc, vs, ctx_len=w.ctx_len,
                             rows_per_group=rows_per_group, n_splits=S, workspace=ws)
-
-    def reduce():
+        if not paths:
+            paths.append(ops.last_path())
+        if e and (i % 2 == 0 or steps < 2):
+            e[1].record()
         ops.reduce_partials(ws, w.n_rows, w.n_q_heads, w.head_dim, S, out=out)
+        if e:
+            e[2].record()
 
-    for i in range(warmup):
-        call(i)
-        reduce()
-    call(0)
-    path = ops.last_path()
-    torch.cuda.synchronize()
-    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    ev = [[E() for _ in range(3)] for _ in range(steps)]
-    torch.cuda._sleep(int(2.4e9 * (0.05e-3 * steps + 0.02)))
-    # (as in the main run: the kernel alone on odd steps, the whole call on even ones)
-    for i in range(steps):
-        ev[i][0].record()
-        call(i + 1)
-        if i % 2 == 1 or steps < 2:
-            ev[i][1].record()
-        reduce()
-        ev[i][2].record()
-    torch.cuda.synchronize()
+    call(0, None)
+    path = paths[0]
+    ev = timed_calls(call, steps, warmup, hold, marks=3)
     odd = [e for i, e in enumerate(ev) if i % 2 == 1 or steps < 2]
     even = [e for i, e in enumerate(ev) if i % 2 == 0]
     k1 = float(np.mean([e[0].elapsed_time(e[1]) for e in odd])) * 1e-3
@@ -678,6 +861,7 @@ def sweep(args):
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     steps = min(args.steps, 30)
+    hold = Hold(ops, dev)
     for hq, hkv, hd, ctx in SWEEP_SHAPES:
         w = W.VerifyWorkload(f"sweep_hd{hd}_ctx{ctx}", hq, hkv, hd, ctx, SWEEP_ROWS, SWEEP_ROWS)
         inp = W.generate(w)
@@ -689,7 +873,7 @@ def sweep(args):
         torch.cuda.synchronize()
         cells = {}
         for rg in SWEEP_GROUPS:
-            k1, k2, S, path = time_verify(ops, bufs, w, rg, steps, args.warmup)
+            k1, k2, S, path = time_verify(ops, bufs, w, rg, steps, args.warmup, hold)
             cells[rg] = (k1, k2, S, path)
         t1 = cells[1][0] + cells[1][1]
         for rg in SWEEP_GROUPS:

@@ -44,9 +44,17 @@ def errors(got, ref):
     return e_row, e_scale
 
 
+# (test id, what, E_row, E_scale) of every comparison in this session, for the
+# terminal summary
+PARITY = []
+
+
 def assert_parity(got, ref, what: str, e_row_tol=E_ROW_TOL, e_scale_tol=E_SCALE_TOL):
+    import os
+
     e_row, e_scale = errors(got, ref)
     note(f"  {what}: E_row={e_row:.3e} E_scale={e_scale:.3e}")
+    PARITY.append((os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0], what, e_row, e_scale))
     assert np.all(np.isfinite(np.asarray(got))), f"{what}: non-finite output"
     assert e_row <= e_row_tol, f"{what}: E_row {e_row:.3e} > {e_row_tol}"
     assert e_scale <= e_scale_tol, f"{what}: E_scale {e_scale:.3e} > {e_scale_tol}"

@@ -32,3 +32,32 @@ def test_traffic_is_keyed_to_the_sources(monkeypatch):
 def test_source_hash_is_stable_and_short():
     h = bench.kernel_source_hash()
     assert h == bench.kernel_source_hash() and len(h) == 16
+
+
+def test_issued_mfma_flops_and_kernel_names():
+    import workloads as W
+
+    p = "prompt kvq8 hd256 qf16 tiles6 own rows_per_group8 groups256 kv_heads1"
+    assert bench.kernel_of_path(p) == "attend_own_q8_kernel<false, true, 6>"
+    # fp16 q: 16 QK + 48 PV MFMAs per (16 vectors, 32 keys) = 2,048 FLOP per pair,
+    # twice the algorithmic 4 * 256 = 1,024, plus the masked halves of diagonal tiles
+    r = bench.issued_mfma_flops(W.PROMPT_CHUNK, p) / W.PROMPT_CHUNK.algorithmic_flops()
+    assert 2.0 < r < 2.01
+    v = "verify kvq8 hd256 qf32 tiles2 rows_per_group4 groups1 splits64 kv_heads4"
+    assert bench.kernel_of_path(v) == "attend_q8_kernel<256, true, false, 2>"
+    # fp32 q: 32 + 48 MFMAs per pair of tiles, 24 of 32 vector slots used
+    r = bench.issued_mfma_flops(W.LONG_VERIFY, v) / W.LONG_VERIFY.algorithmic_flops()
+    assert abs(r - 80 * 16384 / 512 / 1024 * 32 / 24) < 1e-3
+
+
+def test_trace_summary_drops_the_first_launches(tmp_path, capsys):
+    head = ('"Kind","Dispatch_Id","Kernel_Name","Start_Timestamp","End_Timestamp",'
+            '"Workgroup_Size_X","Grid_Size_X","Grid_Size_Y","Grid_Size_Z"\n')
+    rows = [f'"KERNEL_DISPATCH",{i},"k",{1000 * i},{1000 * i + (9000 if i < 2 else 2000)},512,1024,1,1\n'
+            for i in range(6)]
+    f = tmp_path / "t_kernel_trace.csv"
+    f.write_text(head + "".join(rows))
+    bench.summarize_trace(str(f), 2)
+    out = capsys.readouterr().out
+    line = [l for l in out.splitlines() if l.startswith("| `k`")][0]
+    assert "| 4 (6) | 2.00 | 2.00 | 2.00 | 2.00 |" in line

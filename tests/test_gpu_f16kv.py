@@ -27,7 +27,7 @@ def test_verify_f16kv_workloads(name, rg):
     got = ops.verify_f16kv(q, k, v, ctx_len=w.ctx_len, rows_per_group=rg).cpu().numpy()
     note(f"  path: {ops.last_path()}")
     ref = oracle.verify_f16kv(inp.q, inp.k, inp.v, w.ctx_len)
-    assert_parity(got, ref, name)
+    assert_parity(got, ref, f"workload {name} over an fp16 cache (full size, rows_per_group {rg})")
 
 
 SMALL = [
@@ -73,7 +73,7 @@ def test_prompt_f16kv_chunk():
     got = ops.prompt_f16kv(q, k, v, q_pos0=w.pos0, kv_len=w.kv_len).cpu().numpy()
     note(f"  path: {ops.last_path()}")
     ref = oracle.prompt_f16kv(inp.q, inp.k, inp.v, w.pos0)
-    assert_parity(got, ref, "prompt chunk (whole chunk)")
+    assert_parity(got, ref, "prompt_chunk over an fp16 cache (whole chunk)")
 
 
 @pytest.mark.parametrize("hq,hkv,hd,kv_len,n,qd", [

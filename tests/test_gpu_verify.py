@@ -56,7 +56,7 @@ def test_workload_parity(name, rg):
     inp, got, path = run_verify(w, rows_per_group=rg)
     note(f"  path: {path}")
     ref = oracle_verify(inp, w)
-    assert_parity(got, ref, name)
+    assert_parity(got, ref, f"workload {name} (full size, rows_per_group {rg})")
 
 
 SMALL = [
