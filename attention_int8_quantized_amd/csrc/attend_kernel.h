@@ -243,6 +243,56 @@ struct TileCopier {
   }
 };
 
+// SH consecutive shares (of NW) of a tile's copies, issued by one wave.
+template <class L, int NW, int SH>
+struct Copiers {
+  TileCopier<L, NW> c[SH];
+
+  __device__ __forceinline__ void init(__amdgpu_buffer_rsrc_t kc, __amdgpu_buffer_rsrc_t vc,
+                                       __amdgpu_buffer_rsrc_t ks, __amdgpu_buffer_rsrc_t vs, int first,
+                                       int lane) {
+#pragma unroll
+    for (int s = 0; s < SH; ++s) {
+      c[s].kc = kc;
+      c[s].vc = vc;
+      c[s].ks = ks;
+      c[s].vs = vs;
+      c[s].init(first + s, lane);
+    }
+  }
+  __device__ __forceinline__ int count() const {
+    int n = 0;
+#pragma unroll
+    for (int s = 0; s < SH; ++s) n += c[s].count();
+    return n;
+  }
+  __device__ __forceinline__ void issue(uint32_t lds, int key0, bool live) const {
+#pragma unroll
+    for (int s = 0; s < SH; ++s) c[s].issue(lds, key0, live);
+  }
+  __device__ __forceinline__ void issue_part(uint32_t lds, int key0, bool live, int part, int nparts) const {
+#pragma unroll
+    for (int s = 0; s < SH; ++s) c[s].issue_part(lds, key0, live, part, nparts);
+  }
+  // this wave's copies of all but the newest `newer` tiles landed
+  template <int newer>
+  __device__ __forceinline__ void wait_all_but() const {
+    if constexpr (SH == 1) {
+      c[0].template wait_all_but<newer>();
+    } else {
+      switch (count()) {  // wave-uniform
+#define ATTNQ8_WAIT_CASE(k) \
+  case k: wait_vmcnt<(k) * newer>(); break;
+        ATTNQ8_WAIT_CASE(1) ATTNQ8_WAIT_CASE(2) ATTNQ8_WAIT_CASE(3) ATTNQ8_WAIT_CASE(4)
+        ATTNQ8_WAIT_CASE(5) ATTNQ8_WAIT_CASE(6) ATTNQ8_WAIT_CASE(7) ATTNQ8_WAIT_CASE(8)
+        ATTNQ8_WAIT_CASE(9) ATTNQ8_WAIT_CASE(10) ATTNQ8_WAIT_CASE(11) ATTNQ8_WAIT_CASE(12)
+#undef ATTNQ8_WAIT_CASE
+        default: wait_vmcnt<0>(); break;
+      }
+    }
+  }
+};
+
 // One key's NB fp16 block scales, read from LDS as a single vector.
 template <int NB> struct ScaleRow;
 template <> struct ScaleRow<8> {
@@ -335,31 +385,74 @@ __device__ __forceinline__ void fold_scale(Acc& O, const int (&sh)[NBL], int sig
   }
 }
 
+// K units k0, k0 + step, ... (unit k: block k >> 1, 16-key subtile k & 1) of the
+// ring stage `st` -> K fragments in `kf`: every read is issued before the
+// first conversion, so their latencies overlap.
+template <int HD, int STEP>
+__device__ __forceinline__ void convert_k_share(int k0, const uint8_t* st, uint8_t* kf, int lane) {
+  using L = Stage<HD>;
+  constexpr int NU = 2 * L::NB;
+  static_assert(NU % STEP == 0, "units split evenly");
+  constexpr int N = NU / STEP;
+  const int h4 = lane >> 4;
+  uint2 w[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    const int k = k0 + STEP * j;
+    const int c = 2 * (k >> 1) + (h4 >> 1);
+    const int key = 16 * (k & 1) + (lane & 15);
+    w[j] = *(const uint2*)(st + L::K_OFF + key * HD + 16 * chunk_slot<HD>(key, c) + 8 * (h4 & 1));
+  }
+#pragma unroll
+  for (int j = 0; j < N; ++j)
+    *(half8_t*)(kf + ((k0 + STEP * j) * 64 + lane) * 16) = codes8_to_f16(w[j].x, w[j].y);
+}
+
+// What convert_v reads of block b (dim tiles 2b, 2b+1) from the ring stage
+// `st`: the lane's eight per-key V scales (keys pi(h4, e)) and its two
+// transposing reads of the codes (lane 16h + 2k + s addresses key pi(h, k),
+// dims 16d + 8s).
+struct VLoad {
+  half8_t sc;
+  v2i32_t w[2];
+};
+template <int HD>
+__device__ __forceinline__ VLoad load_v(int b, const uint8_t* st, int lane) {
+  using L = Stage<HD>;
+  constexpr int NB = L::NB;
+  const int h4 = lane >> 4;
+  VLoad r;
+  const half_t* vsc = (const half_t*)(st + L::VS_OFF);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r.sc[e] = vsc[pi_key(h4, e) * NB + b];
+  const int vkey = pi_key(h4, (lane & 15) >> 1);
+  const uint8_t* vrow = st + L::V_OFF + vkey * HD + 8 * (lane & 1);
+#pragma unroll
+  for (int dd = 0; dd < 2; ++dd)
+    r.w[dd] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (__attribute__((address_space(3))) v2i32_t*)(vrow + 16 * chunk_slot<HD>(vkey, 2 * b + dd)));
+  return r;
+}
+
+// codes -> exact fp16, times the (possibly shifted) scales -> V^T fragments as
+// exact fp16 hi + lo pairs.
+__device__ __forceinline__ void fold_v(const v2i32_t (&w)[2], half8_t sc, half8_t (&vh)[2], half8_t (&vl)[2]) {
+#pragma unroll
+  for (int dd = 0; dd < 2; ++dd) {
+    const half8_t c = codes8_to_f16((uint32_t)w[dd][0], (uint32_t)w[dd][1]);
+    vh[dd] = c * sc;
+    vl[dd] = __builtin_elementwise_fma(c, sc, -vh[dd]);
+  }
+}
+
 // V codes of block b (dim tiles 2b, 2b+1) of the ring stage `st`, times their
 // per-key scales -> V^T fragments as exact fp16 hi + lo pairs in registers.
 // Returns the block's fold shift (wave-uniform; 0 unless a scale exceeds 512).
 template <int HD>
 __device__ __forceinline__ int convert_v(int b, const uint8_t* st, int lane, half8_t (&vh)[2], half8_t (&vl)[2]) {
-  using L = Stage<HD>;
-  constexpr int NB = L::NB;
-  const int h4 = lane >> 4;
-  // per-key V scales of block b for keys pi(h4, e)
-  const half_t* vsc = (const half_t*)(st + L::VS_OFF);
-  half8_t sc;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) sc[e] = vsc[pi_key(h4, e) * NB + b];
-  // transposing reads: lane 16h + 2k + s addresses key pi(h, k), dims 16d + 8s
-  const int vkey = pi_key(h4, (lane & 15) >> 1);
-  const uint8_t* vrow = st + L::V_OFF + vkey * HD + 8 * (lane & 1);
-  const int s = v_fold_prescale(sc);
-#pragma unroll
-  for (int dd = 0; dd < 2; ++dd) {
-    const v2i32_t w = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-        (__attribute__((address_space(3))) v2i32_t*)(vrow + 16 * chunk_slot<HD>(vkey, 2 * b + dd)));
-    const half8_t c = codes8_to_f16((uint32_t)w[0], (uint32_t)w[1]);
-    vh[dd] = c * sc;
-    vl[dd] = __builtin_elementwise_fma(c, sc, -vh[dd]);
-  }
+  VLoad r = load_v<HD>(b, st, lane);
+  const int s = v_fold_prescale(r.sc);
+  fold_v(r.w, r.sc, vh, vl);
   return s;
 }
 
@@ -395,17 +488,24 @@ __device__ __forceinline__ void read_v16(int b, const uint8_t* st, int lane, hal
 // one vector tile each for QK and do nothing else; waves 4..7 own the 32-dim
 // blocks for PV (two each at head_dim 256; at 64 a block for half the vector
 // tiles) and issue the tile copies, so that the QK waves' loads of q do not
-// queue behind those; K is converted by wave 3 when it owns no vector tile
-// (SIMD 3 hosts no QK work), else by the PV waves.  With eight vector tiles
+// queue behind those; in an instance for two or three vector tiles K is
+// converted by the waves 2..3 or 3, which own none, in one for four by the PV
+// waves.  With eight vector tiles
 // (NQ == 8: prompt blocks) every wave owns a block (or a block for a share of
 // the vector tiles) for PV, converts K and issues copies, and the first nq
 // waves also own a vector tile for QK.
 constexpr int kWaves = 8;
 
-template <int HD, int NQ>
+// Waves per workgroup of an attention-body instance: twelve (three per SIMD,
+// one 32-dim block per PV wave) for row groups of two or three vector tiles at
+// head_dim 256 over an int8 cache, else eight.
+template <int HD, int NQ, bool KV16>
+constexpr int body_waves() { return (!KV16 && HD == 256 && (NQ == 2 || NQ == 3)) ? 12 : kWaves; }
+
+template <int HD, int NQ, bool KV16 = false>
 struct Roles {
   static constexpr bool SPLIT = NQ <= 4;
-  static constexpr int NW = kWaves;
+  static constexpr int NW = body_waves<HD, NQ, KV16>();
   static constexpr int PV0 = SPLIT ? 4 : 0;  // first PV wave
   static constexpr int NPV = NW - PV0;       // PV waves
   static constexpr int NB = Stage<HD>::NB;
@@ -418,12 +518,25 @@ struct Roles {
   __device__ static int block(int wave, int j) { return wave >= PV0 ? (wave - PV0) % NB + NPV * j : NB; }
   // first vector tile of the wave's PV share (then every GW-th)
   __device__ static int qtile0(int wave) { return (wave - PV0) / NB; }
-  // waves that issue the tile copies, and this wave's index among them (< 0: none)
-  static constexpr int NWI = NPV;
-  __device__ static int copy_index(int wave) { return wave - PV0; }
   // waves that convert K, and this wave's index among them (< 0: none)
-  __device__ static int k_workers(int nq) { return SPLIT && nq < 4 ? 1 : NPV; }
-  __device__ static int k_index(int wave, int nq) { return SPLIT && nq < 4 ? (wave == 3 ? 0 : -1) : wave - PV0; }
+  // (an instance for fewer than four vector tiles: waves NQ..3, which own none;
+  // else the PV waves)
+  static constexpr bool K_ON_QK_SIDE = SPLIT && NQ < 4;
+  static constexpr int KW = K_ON_QK_SIDE ? 4 - NQ : NPV;
+  __device__ static int k_workers(int) { return KW; }
+  __device__ static int k_index(int wave, int) {
+    return K_ON_QK_SIDE ? (wave >= NQ && wave < 4 ? wave - NQ : -1) : wave - PV0;
+  }
+  // waves that issue the tile copies: in the instance for two vector tiles
+  // over an int8 cache the K-converting waves 2 and 3, two of four copy shares
+  // each (the PV waves then only convert V and multiply); else the PV waves,
+  // one share each.  copy_index: the wave's first share (< 0: none).
+  static constexpr bool COPY_ON_K = !KV16 && K_ON_QK_SIDE && NQ == 2;
+  static constexpr int NWI = COPY_ON_K ? 4 : NPV;
+  static constexpr int SHARES = COPY_ON_K ? 4 / KW : 1;
+  __device__ static int copy_index(int wave) {
+    return COPY_ON_K ? (wave >= NQ && wave < 4 ? (wave - NQ) * SHARES : -1) : wave - PV0;
+  }
 };
 
 // HD: head dim; QF32: q given in fp32 (else fp16); FINAL: write the normalised
@@ -432,7 +545,7 @@ struct Roles {
 template <int HD, bool QF32, bool FINAL, int NQ, bool KV16>
 __device__ __forceinline__ void attend_body(const AttendArgs& a) {
   using L = std::conditional_t<KV16, Stage16<HD>, Stage<HD>>;
-  using R = Roles<HD, NQ>;
+  using R = Roles<HD, NQ, KV16>;
   constexpr int NW = R::NW;
   constexpr int NB = L::NB;
   // ring stages: tiles t (QK, V), t+1 (K conversion) and the copies in
@@ -496,14 +609,17 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
   const size_t head_rows = (size_t)g * a.kv_stride;
   constexpr int NWI = R::NWI;
   const bool copies = R::copy_index(wave) >= 0;  // wave-uniform
-  TileCopier<L, NWI> cp;
-  cp.kc = make_rsrc((const int8_t*)a.kc + head_rows * L::ROW, k_end * L::ROW);
-  cp.vc = make_rsrc((const int8_t*)a.vc + head_rows * L::ROW, k_end * L::ROW);
-  if constexpr (!KV16) {
-    cp.ks = make_rsrc(a.ks + head_rows * NB, k_end * NB * 2);
-    cp.vs = make_rsrc(a.vs + head_rows * NB, k_end * NB * 2);
+  Copiers<L, NWI, R::SHARES> cp;
+  {
+    const auto kc = make_rsrc((const int8_t*)a.kc + head_rows * L::ROW, k_end * L::ROW);
+    const auto vc = make_rsrc((const int8_t*)a.vc + head_rows * L::ROW, k_end * L::ROW);
+    auto ks = kc, vs = vc;  // (unused over an fp16 cache)
+    if constexpr (!KV16) {
+      ks = make_rsrc(a.ks + head_rows * NB, k_end * NB * 2);
+      vs = make_rsrc(a.vs + head_rows * NB, k_end * NB * 2);
+    }
+    cp.init(kc, vc, ks, vs, copies ? R::copy_index(wave) : NWI, lane);
   }
-  cp.init(copies ? R::copy_index(wave) : NWI, lane);
   const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
   auto issue_first = [&](int n0, int n1) {
     if (copies) {
@@ -833,26 +949,25 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
   // output.
   if constexpr (R::SPLIT) {
     if (wave < R::PV0) {
-      // ---- QK waves (and wave 3 converting K when it owns no vector tile)
+      // ---- QK waves (and the waves among 0..3 without a vector tile, converting K)
       int slot = 0;  // ring stage of tile t
       for (int t = t_begin; t <= t_end; ++t) {
-        __syncthreads();  // K(t) converted; P(t-2) consumed
+        // (copying waves: their copies of tile t+1 landed)
+        if (R::COPY_ON_K && copies && t + 1 < t_end) cp.template wait_all_but<WAIT_NEWER>();
+        __syncthreads();  // K(t) converted; P(t-2) consumed; tile t+1 landed
         const uint8_t* st = ring + slot * L::BYTES;
         const uint8_t* stn = ring + ((slot + 1) % D) * L::BYTES;
+        if (R::COPY_ON_K && copies && t < t_end)
+          cp.issue(ring0 + ((slot + LEAD) % D) * L::BYTES, (t + LEAD) * 32, t + LEAD < t_end);
         if (qk && t < t_end) {
           qk_tile(t, st, [] {});
-        } else if (!KV16 && ki == 0 && t + 1 < t_end) {
-          if constexpr (!KV16) {
-            uint8_t* kfn = kfrag[(t + 1) & 1];
-            constexpr int KB = 2 * NB < 4 ? 2 * NB : 4;  // units per batch (registers)
-#pragma unroll 1
-            for (int k0 = 0; k0 < 2 * NB; k0 += KB)
-#pragma unroll
-              for (int j = 0; j < KB; ++j) convert_k<HD>((k0 + j) >> 1, (k0 + j) & 1, stn, kfn, lane);
-          }
+        } else if (!KV16 && R::K_ON_QK_SIDE && ki >= 0 && t + 1 < t_end) {
+          if constexpr (!KV16 && R::K_ON_QK_SIDE) convert_k_share<HD, R::KW>(ki, stn, kfrag[(t + 1) & 1], lane);
         }
         slot = (slot + 1 == D) ? 0 : slot + 1;
       }
+      // copies into the ring past the last tile may still be landing
+      if (R::COPY_ON_K && copies) wait_vmcnt<0>();
       if (qk) {
         const float l_tot = wave_sum_groups(l_part);
         if (h4 == 0) ml_s[wave][n16] = make_float2(m_ref, l_tot);
@@ -876,21 +991,14 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
       for (int t = t_begin; t <= t_end; ++t) {
         const bool has_qk = t < t_end;
         // this wave's copies of tile t+1 (int8: K converted now) or t landed
-        if (KV16 ? has_qk : t + 1 < t_end) cp.template wait_all_but<WAIT_NEWER>();
+        if (copies && (KV16 ? has_qk : t + 1 < t_end)) cp.template wait_all_but<WAIT_NEWER>();
         __syncthreads();  // K(t) converted; P(t-1) written; tile t+1 landed
         const uint32_t cdst = ring0 + ((slot + LEAD) % D) * L::BYTES;
         const uint8_t* st = ring + slot * L::BYTES;
         const uint8_t* stn = ring + ((slot + 1) % D) * L::BYTES;
         uint8_t* kfn = kfrag[(t + 1) & 1];
         auto kconv = [&]() {
-          if (!KV16 && kw == R::NPV) {
-#pragma unroll
-            for (int j = 0; j < (2 * NB + R::NPV - 1) / R::NPV; ++j) {
-              const int k = ki + R::NPV * j;
-              if ((2 * NB) % R::NPV == 0 || k < 2 * NB)
-                if constexpr (!KV16) convert_k<HD>(k >> 1, k & 1, stn, kfn, lane);
-            }
-          }
+          if constexpr (!KV16 && !R::K_ON_QK_SIDE) convert_k_share<HD, R::NPV>(ki, stn, kfn, lane);
         };
         // the copies of tile t+LEAD go out one share before each block's V
         half8_t vnh[BPW][2], vnl[BPW][2];
@@ -898,7 +1006,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
         int vn_any = 0;
 #pragma unroll
         for (int jb = 0; jb < BPW; ++jb) {
-          if (has_qk) cp.issue_part(cdst, (t + LEAD) * 32, t + LEAD < t_end, jb, BPW);
+          if (copies && has_qk) cp.issue_part(cdst, (t + LEAD) * 32, t + LEAD < t_end, jb, BPW);
           vns[jb] = 0;
           if constexpr (KV16) read_v16<HD>(R::block(wave, jb), st, lane, vnh[jb]);
           else vns[jb] = convert_v<HD>(R::block(wave, jb), st, lane, vnh[jb], vnl[jb]);
@@ -1062,13 +1170,13 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
 }
 
 template <int HD, bool QF32, bool FINAL, int NQ>
-__global__ __launch_bounds__(64 * kWaves) void attend_q8_kernel(const AttendArgs a) {
+__global__ __launch_bounds__((64 * body_waves<HD, NQ, false>())) void attend_q8_kernel(const AttendArgs a) {
   attend_body<HD, QF32, FINAL, NQ, false>(a);
 }
 
 // The same attention over an fp16 K/V cache (no scales).
 template <int HD, bool QF32, bool FINAL, int NQ>
-__global__ __launch_bounds__(64 * kWaves) void attend_f16kv_kernel(const AttendArgs a) {
+__global__ __launch_bounds__((64 * body_waves<HD, NQ, true>())) void attend_f16kv_kernel(const AttendArgs a) {
   attend_body<HD, QF32, FINAL, NQ, true>(a);
 }
 

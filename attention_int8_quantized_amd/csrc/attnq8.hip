@@ -152,6 +152,21 @@ KernelFn pick_own(int nq) {
   else return nq == 6 ? attend_own_q8_kernel<QF32, FINAL, 6> : nullptr;
 }
 
+// Threads per workgroup of the kernel pick_kernel returns (the own layout: eight waves).
+template <bool KV16>
+int threads_for(int hd, int nq) {
+  if (own_layout(KV16, hd, nq)) return 64 * kWaves;
+  switch (hd) {
+    case 256:
+      switch (nq) {
+        case 2: return 64 * body_waves<256, 2, KV16>();
+        case 3: return 64 * body_waves<256, 3, KV16>();
+        default: return 64 * kWaves;
+      }
+    default: return 64 * kWaves;
+  }
+}
+
 template <bool FINAL, bool KV16 = false>
 KernelFn pick_kernel(int hd, bool qf32, int nq) {
   if (own_layout(KV16, hd, nq)) return qf32 ? pick_own<FINAL, true, KV16>(nq) : pick_own<FINAL, false, KV16>(nq);
@@ -242,7 +257,8 @@ int verify_launch(const void* q, int q_dtype, const void* k, const uint16_t* k_s
   a.n_splits = S;
   const float scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)head_dim));
   a.kmul = (float)((double)scale * kLog2e);
-  hipLaunchKernelGGL(fn, dim3(S, groups, n_kv_heads), dim3(64 * kWaves), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL(fn, dim3(S, groups, n_kv_heads), dim3(threads_for<KV16>(head_dim, nq)), 0,
+                     (hipStream_t)stream, a);
   st = launch_status();
   if (st) return st;
   snprintf(g_last_path, sizeof(g_last_path),
@@ -301,7 +317,8 @@ int prompt_launch(const void* q, int q_dtype, const void* k, const uint16_t* k_s
   a.n_splits = 1;
   const float scale = sm_scale > 0.0f ? sm_scale : (float)(1.0 / sqrt((double)head_dim));
   a.kmul = (float)((double)scale * kLog2e);
-  hipLaunchKernelGGL(fn, dim3(1, groups, n_kv_heads), dim3(64 * kWaves), 0, (hipStream_t)stream, a);
+  hipLaunchKernelGGL(fn, dim3(1, groups, n_kv_heads), dim3(threads_for<KV16>(head_dim, nq)), 0,
+                     (hipStream_t)stream, a);
   st = launch_status();
   if (st) return st;
   snprintf(g_last_path, sizeof(g_last_path),
