@@ -517,12 +517,15 @@ int attn_kv_append_q8(const void* k, const void* v, int x_dtype, int n_tokens, i
   return ATTNQ8_OK;
 }
 
-// Blocks per row of the greedy head: about 2,048 blocks over all rows, at most
-// one 2,048-logit chunk per block, at most kHeadMaxBlocks.
+// Blocks per row of the greedy head: about one block per compute unit over
+// all rows (at most kHeadMaxBlocks per row), each covering at least one quad of
+// four logits per thread.
+constexpr int kHeadBlocks = kTargetCUs;  // about one block per compute unit
 static int head_blocks_per_row(int n_rows, int vocab) {
-  const long long chunks = ((long long)vocab + kHeadChunk - 1) / kHeadChunk;
-  long long b = (2048 + n_rows - 1) / n_rows;
-  if (b > chunks) b = chunks;
+  const long long quads = vocab / 4;
+  long long b = (kHeadBlocks + n_rows - 1) / n_rows;
+  const long long by_size = (quads + kHeadThreads - 1) / kHeadThreads;
+  if (b > by_size) b = by_size;
   if (b > kHeadMaxBlocks) b = kHeadMaxBlocks;
   if (b < 1) b = 1;
   return (int)b;
@@ -530,9 +533,11 @@ static int head_blocks_per_row(int n_rows, int vocab) {
 
 size_t attn_verify_head_workspace_bytes(int n_rows, int vocab) {
   if (n_rows < 1 || n_rows > kHeadMaxRows || vocab < 1) return 0;
-  const int bpr = head_blocks_per_row(n_rows, vocab);
-  // the tickets first, at fixed offsets for every shape, then the block states
-  return kHeadTicketBytes + (size_t)n_rows * bpr * sizeof(HeadState);
+  // the tickets first, at fixed offsets for every shape, then the block
+  // states: n_rows * head_blocks_per_row() <= kHeadBlocks + n_rows - 1 for
+  // every vocab, so the size grows with n_rows and a scratch sized for n rows
+  // serves any call with fewer
+  return kHeadTicketBytes + (size_t)(kHeadBlocks + n_rows) * sizeof(HeadSlot);
 }
 
 int attn_verify_head_greedy(const float* logits, int n_rows, int vocab, long long row_stride,
@@ -550,8 +555,9 @@ int attn_verify_head_greedy(const float* logits, int n_rows, int vocab, long lon
   a.row_stride = row_stride;
   a.vocab = vocab;
   a.blocks_per_row = head_blocks_per_row(n_rows, vocab);
+  a.block_quads = (int)(((long long)(vocab / 4) + a.blocks_per_row - 1) / a.blocks_per_row);
   a.ticket = (unsigned*)workspace;
-  a.part = (HeadState*)((char*)workspace + kHeadTicketBytes);
+  a.slot = (HeadSlot*)((char*)workspace + kHeadTicketBytes);
   a.token = token;
   a.top_prob = top_prob;
   hipLaunchKernelGGL(head_greedy_kernel, dim3(a.blocks_per_row, n_rows), dim3(kHeadThreads), 0,

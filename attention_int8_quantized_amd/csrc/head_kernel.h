@@ -9,26 +9,30 @@
 //   top_prob = 1 / sum_i exp(x[i] - x[token]) over the non-NaN entries
 //              (-inf entries add 0; NaN when no entry is finite)
 //
-// One pass over the logits: every lane keeps an online state (max, index of
-// its first occurrence, sum of exp(x - max) rescaled when the max moves),
-// lanes and waves merge in a fixed pattern, each block writes its state to the
-// scratch and takes a ticket; the block that draws the row's last ticket merges
-// the row's block states in block order, writes the result and puts the ticket
-// back to zero.  The merge order never depends on arrival order, so results are
-// run-to-run bitwise identical.
+// One pass over the logits, about one block per compute unit: a block covers
+// a contiguous range of its row in quads of four logits (16-byte loads when
+// the row starts 16-byte aligned); each lane takes the maximum of its values
+// and the index of its first occurrence, then the sum of exp(x - max) as
+// independent terms; lanes and waves merge in a fixed pattern, each block
+// publishes its state in the scratch as self-validating atomic words and takes
+// a ticket; the block that draws the row's last ticket merges the row's block
+// states in block order, writes the result and clears the slots and the
+// ticket.  The merge order never depends
+// on arrival order, so results are run-to-run bitwise identical.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device_utils.h"
 
 namespace attnq8 {
 
 constexpr int kHeadThreads = 256;
-constexpr int kHeadPerLane = 16;                               // logits per lane per pass
-constexpr int kHeadChunk = kHeadThreads * kHeadPerLane;        // 4,096 logits
+constexpr int kHeadQuads = 8;                                  // quads (4 logits) per lane per pass
 constexpr int kHeadMaxBlocks = 256;                            // blocks per row
 constexpr int kHeadNone = 0x7FFFFFFF;                          // no index yet
 constexpr int kHeadMaxRows = 1024;
@@ -42,12 +46,23 @@ struct HeadState {
   int pad;
 };
 
+// A block's state as published to the last block: three 64-bit words, each
+// the 32-bit value (m, s, idx) with a valid flag in its high half, written and
+// read as single atomic objects, so that a reader that sees the flag also sees
+// that word's value; the reader clears the words after use.
+struct HeadSlot {
+  unsigned long long w[3];
+};
+constexpr unsigned long long kHeadValid = 1ull << 32;
+constexpr int kHeadSpinLimit = 1 << 16;  // bounded wait for a published word
+
 struct HeadArgs {
   const float* logits;  // row r starts at logits + r * row_stride
   long long row_stride;
   int vocab;
   int blocks_per_row;
-  HeadState* part;      // [n_rows][blocks_per_row]
+  int block_quads;      // quads of four logits per block (the last block: the rest)
+  HeadSlot* slot;       // [n_rows][blocks_per_row], all words zero between calls
   unsigned* ticket;     // [n_rows], zero between calls
   int* token;           // [n_rows]
   float* top_prob;      // [n_rows] (may be null)
@@ -104,41 +119,90 @@ __device__ __forceinline__ HeadState head_block_merge(HeadState st, HeadState* l
   return r;
 }
 
+// The state of the values x[0..N) at indices idx[0..N), in increasing index
+// order: the maximum and its first index, then the sum of exp(x - max) over the
+// finite values as independent terms.
+template <int N>
+__device__ __forceinline__ HeadState head_state_of(const float (&x)[N], const int (&idx)[N]) {
+  HeadState st = {-INFINITY, 0.0f, kHeadNone, 0};
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    // a NaN never compares; -inf is an ordinary value (first one wins)
+    if (x[k] > st.m || (x[k] == st.m && st.idx == kHeadNone)) {
+      st.idx = x[k] > st.m || st.idx == kHeadNone ? idx[k] : st.idx;
+      st.m = fmaxf(st.m, x[k]);
+    }
+  }
+  if (st.m != -INFINITY) {
+    float e[N];
+#pragma unroll
+    for (int k = 0; k < N; ++k) e[k] = (x[k] == x[k] && x[k] != -INFINITY) ? head_exp(x[k] - st.m) : 0.0f;
+    // pairwise, in a fixed order
+#pragma unroll
+    for (int w = 1; w < N; w *= 2)
+#pragma unroll
+      for (int k = 0; k + w < N; k += 2 * w) e[k] += e[k + w];
+    st.s = e[0];
+  }
+  return st;
+}
+
 __global__ __launch_bounds__(kHeadThreads) void head_greedy_kernel(HeadArgs a) {
   __shared__ HeadState lds[kHeadThreads / 64];
   __shared__ int last;
   const int row = blockIdx.y;
   const int blk = blockIdx.x;
+  const int lane = threadIdx.x;
   const float* x = a.logits + (long long)row * a.row_stride;
 
+  // quads [q0, q1) of the row; the last block also takes the vocab % 4 tail
+  const long long nq = a.vocab >> 2;
+  const long long q0 = (long long)blk * a.block_quads;
+  const long long q1 = blk == a.blocks_per_row - 1 ? nq : min(nq, q0 + a.block_quads);
   HeadState st = {-INFINITY, 0.0f, kHeadNone, 0};
-  const long long step = (long long)a.blocks_per_row * kHeadChunk;
-  for (long long base = (long long)blk * kHeadChunk; base < a.vocab; base += step) {
-    float v[kHeadPerLane];
+  // 16-byte loads when the row starts 16-byte aligned (block-uniform)
+  auto scan = [&](auto vec) {
+    for (long long base = q0; base < q1; base += (long long)kHeadQuads * kHeadThreads) {
+      float v[4 * kHeadQuads];
+      int vi[4 * kHeadQuads];
 #pragma unroll
-    for (int j = 0; j < kHeadPerLane; ++j) {
-      const long long i = base + j * kHeadThreads + threadIdx.x;
-      v[j] = i < a.vocab ? x[i] : NAN;  // past the row: skipped like a NaN
+      for (int j = 0; j < kHeadQuads; ++j) {
+        const long long q = base + (long long)j * kHeadThreads + lane;
+        float4_t f = {NAN, NAN, NAN, NAN};  // past the range: skipped like NaN
+        if (q < q1) {
+          if constexpr (decltype(vec)::value) f = __builtin_nontemporal_load((const float4_t*)(x + 4 * q));
+          else f = (float4_t){x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]};
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          v[4 * j + c] = f[c];
+          vi[4 * j + c] = (int)(4 * q + c);
+        }
+      }
+      st = head_merge(st, head_state_of(v, vi));
     }
-#pragma unroll
-    for (int j = 0; j < kHeadPerLane; ++j)
-      head_push(st, v[j], (int)(base + j * kHeadThreads + threadIdx.x));
+  };
+  if ((((uintptr_t)x) & 15) == 0) scan(std::true_type());
+  else scan(std::false_type());
+  if (blk == a.blocks_per_row - 1 && lane < (a.vocab & 3)) {
+    float t[1] = {x[4 * nq + lane]};
+    int ti[1] = {(int)(4 * nq + lane)};
+    st = head_merge(st, head_state_of(t, ti));
   }
   st = head_block_merge(st, lds);
 
-  // The block states go out as device-scope atomic stores (written through
-  // to the device's coherence point) and are read back as device-scope atomic
-  // loads, and the state's stores have completed (vmcnt 0) before the ticket
-  // is taken; no full-cache fence is needed.
-  HeadState* part = a.part + (long long)row * a.blocks_per_row;
+  // Hand-off: the block publishes its state as three self-validating atomic
+  // words, then takes a ticket; the block that draws the row's last ticket
+  // reads every slot of the row, waiting (boundedly) for each word's flag --
+  // the writer stored it before taking its ticket, so it arrives -- merges the
+  // states in block order, clears the slots and the ticket for the next call.
+  HeadSlot* slots = a.slot + (long long)row * a.blocks_per_row;
   if (threadIdx.x == 0) {
-    HeadState* p = part + blk;
-    __hip_atomic_store(&p->m, st.m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&p->s, st.s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&p->idx, st.idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    wait_vmcnt<0>();
-    const unsigned t =
-        __hip_atomic_fetch_add(&a.ticket[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    HeadSlot* p = slots + blk;
+    __hip_atomic_store(&p->w[0], kHeadValid | __float_as_uint(st.m), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&p->w[1], kHeadValid | __float_as_uint(st.s), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&p->w[2], kHeadValid | (uint32_t)st.idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned t = __hip_atomic_fetch_add(&a.ticket[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     last = t == (unsigned)a.blocks_per_row - 1;
   }
   __syncthreads();
@@ -147,17 +211,27 @@ __global__ __launch_bounds__(kHeadThreads) void head_greedy_kernel(HeadArgs a) {
   // the last block of the row: merge the row's block states in block order
   HeadState r = {-INFINITY, 0.0f, kHeadNone, 0};
   if ((int)threadIdx.x < a.blocks_per_row) {
-    HeadState* p = part + threadIdx.x;
-    r.m = __hip_atomic_load(&p->m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    r.s = __hip_atomic_load(&p->s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    r.idx = __hip_atomic_load(&p->idx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    HeadSlot* p = slots + threadIdx.x;
+    unsigned long long w[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) w[k] = __hip_atomic_load(&p->w[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int spin = 0; !(w[0] & w[1] & w[2] & kHeadValid) && spin < kHeadSpinLimit; ++spin) {
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+        if (!(w[k] & kHeadValid)) w[k] = __hip_atomic_load(&p->w[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) __hip_atomic_store(&p->w[k], 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    r.m = __uint_as_float((uint32_t)w[0]);
+    r.s = __uint_as_float((uint32_t)w[1]);
+    r.idx = (int)(uint32_t)w[2];
   }
   __syncthreads();  // lds is reused
   r = head_block_merge(r, lds);
   if (threadIdx.x == 0) {
     a.token[row] = r.idx == kHeadNone ? -1 : r.idx;
     if (a.top_prob) a.top_prob[row] = r.m == -INFINITY ? NAN : 1.0f / r.s;
-    a.ticket[row] = 0u;  // ready for the next call
+    __hip_atomic_store(&a.ticket[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
   }
 }
 

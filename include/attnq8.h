@@ -236,10 +236,11 @@ int attn_kv_append_q8(const void* k, const void* v, int x_dtype,
  * in elements; 4-byte alignment); token int32 [n_rows]; top_prob fp32
  * [n_rows] or NULL.  The workspace (16-byte aligned, at least
  * attn_verify_head_workspace_bytes(n_rows, vocab) bytes) holds one ticket per
- * row at fixed offsets in its first 4,096 bytes, then per-block states: it
- * must be zero-filled before its first use, and every completed call leaves
- * the tickets at zero again, so one workspace (sized for the largest call)
- * serves any sequence of calls of any shape on one stream.  Calls that share
+ * row at fixed offsets in its first 4,096 bytes, then per-block states (24
+ * bytes each, for about 256 blocks over all rows): it must be zero-filled
+ * before its first use, and every completed call leaves it zero again, so one
+ * workspace (sized for the largest call; the size grows with n_rows) serves
+ * any sequence of calls of any shape on one stream.  Calls that share
  * a workspace must not run concurrently.  1 <= n_rows <= 1024, vocab >= 1.
  * ------------------------------------------------------------------------- */
 size_t attn_verify_head_workspace_bytes(int n_rows, int vocab);

@@ -172,12 +172,16 @@ def test_kv_append_rejects_before_launch(lib, kw, status):
 
 def test_head_workspace_bytes(lib):
     f = lib.attn_verify_head_workspace_bytes
-    # 4,096 bytes of tickets, then 16 bytes per block; 248,320 logits = 61
-    # chunks of 4,096: one chunk per block for 1..33 rows
-    assert f(1, 248320) == 4096 + 61 * 16
-    assert f(5, 248320) == 4096 + 5 * 61 * 16
-    assert f(64, 248320) == 4096 + 64 * 32 * 16   # 2,048 blocks over all rows
-    assert f(1, 1) == 4096 + 16
+    # 4,096 bytes of tickets, then 24 bytes per block state: about 256 blocks
+    # over all rows (ceil(256 / rows) per row), sized for 256 + rows states so
+    # that the size grows with the row count
+    assert f(1, 248320) == 4096 + 257 * 24
+    assert f(5, 248320) == 4096 + 261 * 24
+    assert f(64, 248320) == 4096 + 320 * 24
+    assert f(1, 1) == 4096 + 257 * 24
+    assert all(f(n, 248320) <= f(n + 1, 248320) for n in range(1, 1024))
+    for n in (1, 3, 5, 7, 64, 100, 255, 257, 1024):  # rows * ceil(256 / rows) states fit
+        assert n * -(-256 // n) * 24 <= f(n, 248320) - 4096
     assert f(0, 100) == 0 and f(3, 0) == 0 and f(1025, 100) == 0
 
 

@@ -98,9 +98,11 @@ def test_head_workspace_reuse_and_determinism():
                 assert np.array_equal(top.view(np.uint32), first[2].view(np.uint32))
 
 
-def test_head_row_stride():
-    V, S = 10000, 10240
-    rng = np.random.default_rng(44)
+@pytest.mark.parametrize("V,S", [(10000, 10240), (10001, 10003), (248320, 248321)])
+def test_head_row_stride(V, S):
+    """Rows at a stride (16-byte aligned rows and rows that are not: the
+    kernel's vector and scalar loads), padding beyond each row ignored."""
+    rng = np.random.default_rng(44 + V)
     buf = (rng.standard_normal((3, S)) * 2).astype(np.float32)
     buf[:, V:] = 1e9  # padding beyond the row must be ignored
     t = torch.from_numpy(buf).cuda()[:, :V]
