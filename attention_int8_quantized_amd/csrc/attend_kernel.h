@@ -777,16 +777,37 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
           }
       }
     } else {
+    // (split instances: the fragments and scales of group b0 + KG are
+    // requested before the products of group b0, so that their latency hides
+    // behind those; the others have no registers to spare for that)
+    constexpr bool AHEAD = R::SPLIT;
+    half8_t kvn[2][KG];
+    ScaleRow<KG> dkn[2][4];
+    auto load_group = [&](int b0) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int j = 0; j < KG; ++j) kvn[u][j] = *(const half8_t*)(kf + (((b0 + j) * 2 + u) * 64 + lane) * 16);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dkn[u][e].load(Kst + (16 * u + 4 * h4 + e) * NB + b0);
+      }
+    };
+    if (AHEAD) load_group(0);
 #pragma unroll
     for (int b0 = 0; b0 < NB; b0 += KG) {
       half8_t kv[2][KG];
       ScaleRow<KG> dk[2][4];
+      if (!AHEAD) load_group(b0);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int j = 0; j < KG; ++j) kv[u][j] = *(const half8_t*)(kf + (((b0 + j) * 2 + u) * 64 + lane) * 16);
+        for (int j = 0; j < KG; ++j) kv[u][j] = kvn[u][j];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dk[u][e].load(Kst + (16 * u + 4 * h4 + e) * NB + b0);
+        for (int e = 0; e < 4; ++e) dk[u][e] = dkn[u][e];
+      }
+      if (AHEAD && b0 + KG < NB) {
+        load_group(b0 + KG);
+        asm volatile("" ::: "memory");  // (those loads stay ahead of these products)
       }
       float4_t acc[2][KG];
 #pragma unroll
