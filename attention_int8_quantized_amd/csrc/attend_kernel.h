@@ -970,25 +970,33 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
   // output.
   if constexpr (R::SPLIT) {
     if (wave < R::PV0) {
-      // ---- QK waves (and the waves among 0..3 without a vector tile, converting K)
-      int slot = 0;  // ring stage of tile t
-      for (int t = t_begin; t <= t_end; ++t) {
-        // (copying waves: their copies of tile t+1 landed)
-        if (R::COPY_ON_K && copies && t + 1 < t_end) cp.template wait_all_but<WAIT_NEWER>();
-        __syncthreads();  // K(t) converted; P(t-2) consumed; tile t+1 landed
-        const uint8_t* st = ring + slot * L::BYTES;
-        const uint8_t* stn = ring + ((slot + 1) % D) * L::BYTES;
-        if (R::COPY_ON_K && copies && t < t_end)
-          cp.issue(ring0 + ((slot + LEAD) % D) * L::BYTES, (t + LEAD) * 32, t + LEAD < t_end);
-        if (qk && t < t_end) {
-          qk_tile(t, st, [] {});
-        } else if (!KV16 && R::K_ON_QK_SIDE && ki >= 0 && t + 1 < t_end) {
-          if constexpr (!KV16 && R::K_ON_QK_SIDE) convert_k_share<HD, R::KW>(ki, stn, kfrag[(t + 1) & 1], lane);
+      // ---- QK waves (and the waves among 0..3 without a vector tile,
+      // converting K), in loops of their own: neither carries the other's
+      // bookkeeping
+      if (qk) {
+        int slot = 0;  // ring stage of tile t
+        for (int t = t_begin; t <= t_end; ++t) {
+          __syncthreads();  // K(t) converted; P(t-2) consumed; tile t+1 landed
+          if (t < t_end) qk_tile(t, ring + slot * L::BYTES, [] {});
+          slot = (slot + 1 == D) ? 0 : slot + 1;
         }
-        slot = (slot + 1 == D) ? 0 : slot + 1;
+      } else {
+        int slot = 0;  // ring stage of tile t
+        for (int t = t_begin; t <= t_end; ++t) {
+          // (copying waves: their copies of tile t+1 landed)
+          if (R::COPY_ON_K && copies && t + 1 < t_end) cp.template wait_all_but<WAIT_NEWER>();
+          __syncthreads();  // K(t) converted; P(t-2) consumed; tile t+1 landed
+          const uint8_t* stn = ring + ((slot + 1) % D) * L::BYTES;
+          if (R::COPY_ON_K && copies && t < t_end)
+            cp.issue(ring0 + ((slot + LEAD) % D) * L::BYTES, (t + LEAD) * 32, t + LEAD < t_end);
+          if constexpr (!KV16 && R::K_ON_QK_SIDE) {
+            if (ki >= 0 && t + 1 < t_end) convert_k_share<HD, R::KW>(ki, stn, kfrag[(t + 1) & 1], lane);
+          }
+          slot = (slot + 1 == D) ? 0 : slot + 1;
+        }
+        // copies into the ring past the last tile may still be landing
+        if (R::COPY_ON_K && copies) wait_vmcnt<0>();
       }
-      // copies into the ring past the last tile may still be landing
-      if (R::COPY_ON_K && copies) wait_vmcnt<0>();
       if (qk) {
         const float l_tot = wave_sum_groups(l_part);
         if (h4 == 0) ml_s[wave][n16] = make_float2(m_ref, l_tot);
@@ -998,6 +1006,9 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
       // ---- PV waves: copies, K units of tile t+1 (unconditionally: past the
       // last tile the result is never read; only when wave 3 does not convert
       // K), V^T of tile t into registers for the next iteration, PV of tile t-1
+      // (no copies here when the K-converting waves issue them: known at
+      // compile time, so the loop carries none of their bookkeeping)
+      const bool pv_copies = !R::COPY_ON_K && copies;
       float4_t O[BPW][NQW][2];
 #pragma unroll
       for (int jb = 0; jb < BPW; ++jb)
@@ -1012,7 +1023,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
       for (int t = t_begin; t <= t_end; ++t) {
         const bool has_qk = t < t_end;
         // this wave's copies of tile t+1 (int8: K converted now) or t landed
-        if (copies && (KV16 ? has_qk : t + 1 < t_end)) cp.template wait_all_but<WAIT_NEWER>();
+        if (pv_copies && (KV16 ? has_qk : t + 1 < t_end)) cp.template wait_all_but<WAIT_NEWER>();
         __syncthreads();  // K(t) converted; P(t-1) written; tile t+1 landed
         const uint32_t cdst = ring0 + ((slot + LEAD) % D) * L::BYTES;
         const uint8_t* st = ring + slot * L::BYTES;
@@ -1027,7 +1038,7 @@ __device__ __forceinline__ void attend_body(const AttendArgs& a) {
         int vn_any = 0;
 #pragma unroll
         for (int jb = 0; jb < BPW; ++jb) {
-          if (copies && has_qk) cp.issue_part(cdst, (t + LEAD) * 32, t + LEAD < t_end, jb, BPW);
+          if (pv_copies && has_qk) cp.issue_part(cdst, (t + LEAD) * 32, t + LEAD < t_end, jb, BPW);
           vns[jb] = 0;
           if constexpr (KV16) read_v16<HD>(R::block(wave, jb), st, lane, vnh[jb]);
           else vns[jb] = convert_v<HD>(R::block(wave, jb), st, lane, vnh[jb], vnl[jb]);
