@@ -37,6 +37,15 @@ Prints one JSON line.  Other modes:
                        grouped by kernel and grid, the first --skip-first
                        launches of each group (the warm-up) left out; a
                        markdown table (no GPU)
+  --summarize-pmc F..  per-dispatch means of the counters in rocprofv3 --pmc
+                       counter-collection CSVs, by kernel and grid; a markdown
+                       table (no GPU)
+  --traffic-from DIR   HBM bytes per launch from the FETCH_SIZE and WRITE_SIZE
+                       passes over bench.py and over --copy-calibration (CSVs
+                       under DIR/FETCH_SIZE, DIR/WRITE_SIZE, DIR/FETCH_SIZE_copy,
+                       DIR/WRITE_SIZE_copy), scaled by the copy's known size;
+                       prints a markdown table and, with --write-traffic,
+                       writes profiles/traffic.json for these sources (no GPU)
 """
 
 from __future__ import annotations
@@ -82,6 +91,9 @@ def parse():
                     help="skip the other verify configurations")
     ap.add_argument("--summarize-trace", default=None,
                     help="a rocprofv3 *_kernel_trace.csv to summarise (no GPU)")
+    ap.add_argument("--summarize-pmc", nargs="+", default=None)
+    ap.add_argument("--traffic-from", default=None)
+    ap.add_argument("--write-traffic", action="store_true")
     ap.add_argument("--skip-first", type=int, default=6,
                     help="launches per (kernel, grid) group left out by --summarize-trace")
     return ap.parse_args()
@@ -140,6 +152,12 @@ def main():
         return
     if args.oracle_times:
         oracle_times()
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return
+    if args.traffic_from:
+        traffic_from(args.traffic_from, args.write_traffic)
         return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.skip_first)
@@ -514,6 +532,96 @@ def summarize_trace(path, skip_first):
         short = name if len(name) <= 110 else name[:107] + "..."
         print(f"| `{short}` | {'x'.join(grid)} | {block} | {len(used)} ({n_all}) | "
               f"{statistics.median(used):.2f} | {statistics.mean(used):.2f} | {min(used):.2f} | {max(used):.2f} |")
+
+
+def _pmc_rows(paths):
+    """(kernel, grid threads, counter) -> per-dispatch values, from rocprofv3
+    counter-collection CSVs (files, or directories searched for them)."""
+    import csv
+    import glob
+
+    files = []
+    for p in paths:
+        files += sorted(glob.glob(os.path.join(p, "**", "*counter_collection.csv"), recursive=True)) \
+            if os.path.isdir(p) else [p]
+    out = {}
+    for fn in files:
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                key = (row["Kernel_Name"], int(row["Grid_Size"]), row["Counter_Name"])
+                out.setdefault(key, []).append(float(row["Counter_Value"]))
+    return out
+
+
+def _short_kernel(name):
+    m = re.match(r"(?:void )?(?:attnq8::)?([^(]+)", name)
+    return m.group(1) if m else name
+
+
+def summarize_pmc(paths):
+    rows = _pmc_rows(paths)
+    counters = sorted({c for _, _, c in rows})
+    kernels = sorted({(k, g) for k, g, _ in rows}, key=lambda x: (x[0], x[1]))
+    print("| kernel | grid (threads) | dispatches | " + " | ".join(counters) + " |")
+    print("|---|---|---|" + "---|" * len(counters))
+    for k, g in kernels:
+        vals = [rows.get((k, g, c)) for c in counters]
+        n = max(len(v) for v in vals if v)
+        cells = [f"{np.mean(v):,.4g}" if v else "" for v in vals]
+        print(f"| `{_short_kernel(k)}` | {g:,} | {n} | " + " | ".join(cells) + " |")
+
+
+# traffic.json keys: the kernels bench.py reports `traffic` for (the long
+# verify's reducer is the reduce_partials_kernel<256> launch with the smallest
+# grid among the configurations bench.py times)
+TRAFFIC_KEYS = {
+    "verify": "attend_q8_kernel<256, true, false, 2>",
+    "verify_window": "attend_q8_kernel<256, true, false, 3>",
+    "prompt": "attend_own_q8_kernel<false, true, 6>",
+    "reduce": "reduce_partials_kernel<256>",
+    "append": "kv_append_q8_kernel<true>",
+    "head": "head_greedy_kernel",
+    "verify_f16kv": "attend_f16kv_kernel<256, true, false, 2>",
+    "prompt_f16kv": "attend_own_f16kv_kernel<false, true, 6>",
+}
+
+
+def traffic_from(d, write):
+    fetch = _pmc_rows([os.path.join(d, "FETCH_SIZE")])
+    write_rows = _pmc_rows([os.path.join(d, "WRITE_SIZE")])
+    fetch_c = _pmc_rows([os.path.join(d, "FETCH_SIZE_copy")])
+    write_c = _pmc_rows([os.path.join(d, "WRITE_SIZE_copy")])
+
+    def copy_kib(rows, counter):
+        # the device copy of COPY_BYTES: the largest per-dispatch value of the counter
+        vals = [np.mean(v) for (k, g, c), v in rows.items() if c == counter]
+        return max(vals)
+
+    kib = COPY_BYTES / 1024
+    ff = kib / copy_kib(fetch_c, "FETCH_SIZE")
+    wf = kib / copy_kib(write_c, "WRITE_SIZE")
+    print(f"copy calibration: {COPY_BYTES:,} bytes read and written; FETCH_SIZE factor {ff:.3f}, "
+          f"WRITE_SIZE factor {wf:.3f}")
+    print("| key | kernel | grid (threads) | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB |")
+    print("|---|---|---|---|---|---|---|")
+    kernels = {}
+    for key, short in TRAFFIC_KEYS.items():
+        cands = sorted({g for (k, g, c) in fetch if _short_kernel(k) == short and c == "FETCH_SIZE"})
+        if not cands:
+            continue
+        g = cands[0]
+        name = next(k for (k, gg, c) in fetch if _short_kernel(k) == short and gg == g)
+        fr = float(np.mean(fetch[(name, g, "FETCH_SIZE")]))
+        wr = float(np.mean(write_rows.get((name, g, "WRITE_SIZE"), [float("nan")])))
+        rb, wb = fr * 1024 * ff, wr * 1024 * wf
+        kernels[key] = {"read_bytes": int(rb), "write_bytes": int(wb), "total_bytes": int(rb + wb)}
+        print(f"| {key} | `{short}` | {g:,} | {fr:,.1f} | {wr:,.1f} | {rb / 1e6:.2f} | {wb / 1e6:.2f} |")
+    if write:
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump({"source_hash": kernel_source_hash(), "fetch_factor": round(ff, 4),
+                       "write_factor": round(wf, 4), "kernels": kernels}, f, indent=1)
+            f.write("\n")
+        print(f"wrote {TRAFFIC_FILE} (sources {kernel_source_hash()})")
 
 
 def read_ceiling(ops, dev, nbytes=1 << 30, reps=10):
