@@ -483,14 +483,16 @@ __device__ __forceinline__ void read_v16(int b, const uint8_t* st, int lane, hal
   }
 }
 
-// Work split of a workgroup over its eight waves.  With at most four vector
-// tiles (NQ <= 4: verify row groups) the roles are disjoint: waves 0..3 own
-// one vector tile each for QK and do nothing else; waves 4..7 own the 32-dim
-// blocks for PV (two each at head_dim 256; at 64 a block for half the vector
-// tiles) and issue the tile copies, so that the QK waves' loads of q do not
-// queue behind those; in an instance for two or three vector tiles K is
-// converted by the waves 2..3 or 3, which own none, in one for four by the PV
-// waves.  With eight vector tiles
+// Work split of a workgroup over its waves (eight, or twelve: body_waves).
+// With at most four vector tiles (NQ <= 4: verify row groups) the roles are
+// disjoint: waves 0..NQ-1 own one vector tile each for QK and do nothing
+// else; waves 4.. own the 32-dim blocks for PV (one each with twelve waves;
+// two each at head_dim 256 with eight; at 64 a block for half the vector
+// tiles).  In an instance for two or three vector tiles K is converted by
+// the waves NQ..3, which own no vector tile, in one for four by the PV waves.
+// The tile copies are issued by the K-converting waves in the instance for
+// two vector tiles over an int8 cache, else by the PV waves, so that the QK
+// waves' loads of q never queue behind them.  With eight vector tiles
 // (NQ == 8: prompt blocks) every wave owns a block (or a block for a share of
 // the vector tiles) for PV, converts K and issues copies, and the first nq
 // waves also own a vector tile for QK.
