@@ -110,10 +110,15 @@ int splits_for(int n_keys, int units, int hd) {
   return s;
 }
 
-// Default row group: every row of a KV head in one workgroup, up to 128 query
-// vectors (64 at head_dim 256, where 128 would not fit the registers).
+// Default row group: as many rows of a KV head as fit 64 query vectors (four
+// vector tiles: the split-role instances).  The eight-tile instances hold up
+// to 128, but per call they measured slower at every head_dim than groups of
+// four tiles, which read the context twice as often: at 32 rows of 32 / 8
+// heads, 8,192 keys, 31.6 against 40.8 us at head_dim 128 and 24.5 against
+// 30.1 us at 64 (fp16 cache: 25.1 against 29.2 us).
 int auto_rows_per_group(int G, int n_rows, int hd) {
-  int rg = (hd == 256 ? 64 : kMaxVectorsPerGroup) / G;
+  (void)hd;
+  int rg = 64 / G;
   if (rg > n_rows) rg = n_rows;
   if (rg < 1) rg = 1;
   return rg;

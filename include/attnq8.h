@@ -68,8 +68,9 @@ enum { ATTNQ8_F32 = 0, ATTNQ8_F16 = 1 };
  * group that reads one KV head -- rows_per_group * n_q_heads / n_kv_heads
  * query vectors, at most 128 -- and splits the group's visible context into
  * n_splits ranges of whole 32-key tiles.  rows_per_group = 0 picks the largest
- * group that fits; n_splits = 0 picks attn_verify_q8_splits().  The grouping
- * and split count change only the rounding of the result.
+ * group of at most 64 query vectors (at least one row); n_splits = 0 picks
+ * attn_verify_q8_splits().  The grouping and split count change only the
+ * rounding of the result.
  *
  * Output: split-context partials in `workspace`, merged by
  * attn_reduce_partials().  Workspace layout (fp32, 16-byte aligned):
