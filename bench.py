@@ -15,7 +15,10 @@ in rotating copies of at least 1 GB (four times the 256 MB Infinity Cache)
 so that repeats come from HBM.  Durations come from HIP events recorded on the
 library's stream: around each whole verify call (attention kernel + reducer,
 nothing recorded between them) and each prompt call, and on alternate steps one
-more event after the attention kernel, which times it alone for its roofline.
+more event after the attention kernel, which times it alone in the call.  The
+verify roofline's launch duration comes from a region of the attention kernel
+alone launched back to back after the steps (events around the region divided
+by its launches), so that no per-launch event latency enters it.
 The GPU is held by a spin kernel while the timed launches are queued so that
 host submission latency does not enter them.  The practical HBM read ceiling
 (a plain 1 GiB read by the library's attnq8_stream_read) is reported beside the
@@ -94,6 +97,8 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs="+", default=None)
     ap.add_argument("--traffic-from", default=None)
     ap.add_argument("--write-traffic", action="store_true")
+    ap.add_argument("--tail", type=int, default=0,
+                    help="--summarize-trace: only the last N launches of each group")
     ap.add_argument("--skip-first", type=int, default=6,
                     help="launches per (kernel, grid) group left out by --summarize-trace")
     return ap.parse_args()
@@ -160,7 +165,7 @@ def main():
         traffic_from(args.traffic_from, args.write_traffic)
         return
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.skip_first)
+        summarize_trace(args.summarize_trace, args.skip_first, args.tail)
         return
 
     import torch
@@ -252,6 +257,21 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
+    # The attention kernel alone, launched back to back over the rotating
+    # inputs after the steps: events around the whole region, divided by the
+    # launches in it, give the launch duration of the roofline (a kernel
+    # bracketed by its own events also carries the dispatch latency).
+    KR = max(K, 10)
+    torch.cuda.synchronize()
+    hold(60e-6 * KR + 1e-3)
+    r0, r1 = E(), E()
+    r0.record()
+    for i in range(KR):
+        verify_call(i + 1)
+    r1.record()
+    torch.cuda.synchronize()
+    kr_mean = r0.elapsed_time(r1) / KR * 1e-3  # s
+
     odd = [i for i in range(K) if i % 2 == 1 or K < 2]
     even = [i for i in range(K) if i % 2 == 0]
     k1 = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in odd]) * 1e-3  # s
@@ -266,6 +286,7 @@ def main():
     gbs = vbytes / verify_s / 1e9
     k1_mean = float(np.mean(k1))
     k1_gbs = vbytes / k1_mean / 1e9
+    kr_gbs = vbytes / kr_mean / 1e9
 
     res = {
         "metric": METRIC,
@@ -298,14 +319,17 @@ def main():
             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
             "kernel_gbs": round(k1_gbs, 2),
             "kernel_frac_hbm": round(k1_gbs / HBM_PEAK_GBS, 4),
+            "kernel_us_back_to_back": round(kr_mean * 1e6, 3),
+            "launches_back_to_back": KR,
         },
         "roofline": {
             "kernel": kernel_of_path(verify_path),
             "bound": "hbm",
-            "achieved": round(k1_gbs, 2),
+            "achieved": round(kr_gbs, 2),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
+            "frac": round(kr_gbs / HBM_PEAK_GBS, 4),
+            "launch_us": round(kr_mean * 1e6, 3),
             "traffic": load_traffic("verify"),
         },
     }
@@ -506,9 +530,10 @@ def time_verify_configs(ops, dev, args, steps, hold):
     return out
 
 
-def summarize_trace(path, skip_first):
+def summarize_trace(path, skip_first, tail=0):
     """Per-kernel durations from a rocprofv3 kernel-trace CSV: launches grouped by
-    (kernel, grid), the first skip_first of each group dropped; markdown table."""
+    (kernel, grid), the first skip_first of each group dropped (or, with tail,
+    only the last `tail` kept); markdown table."""
     import csv
     import statistics
 
@@ -526,7 +551,7 @@ def summarize_trace(path, skip_first):
     rows = []
     for (name, grid, block), d in groups.items():
         d.sort()
-        used = [x for _, x in d[skip_first:]] or [x for _, x in d]
+        used = [x for _, x in (d[-tail:] if tail else d[skip_first:])] or [x for _, x in d]
         rows.append((statistics.median(used) * len(used), name, grid, block, used, len(d)))
     for _, name, grid, block, used, n_all in sorted(rows, reverse=True):
         short = name if len(name) <= 110 else name[:107] + "..."
