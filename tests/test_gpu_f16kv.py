@@ -38,9 +38,10 @@ SMALL = [
     (12, 1, 256, 100, 8, 0, 0, np.float32, 17),
     (32, 8, 128, 500, 32, 1, 5, np.float32, 0),
     (16, 2, 64, 1000, 9, 0, 0, np.float16, 0),
-    (64, 1, 128, 70, 2, 0, 0, np.float32, 0),   # 128 vectors in one group
+    (64, 1, 128, 70, 2, 0, 0, np.float32, 0),   # automatic: one row (64 vectors) per group
+    (64, 1, 128, 70, 2, 2, 0, np.float32, 0),   # 128 vectors in one group
     (24, 4, 256, 2000, 8, 0, 63, np.float32, 0),
-    (48, 1, 256, 300, 2, 0, 0, np.float16, 5),  # 96 vectors: the largest group at hd 256
+    (48, 1, 256, 300, 2, 2, 0, np.float16, 5),  # 96 vectors: the largest group at hd 256
     (24, 2, 256, 400, 8, 8, 0, np.float32, 0),   # 96 vectors per group: the own layout
     (24, 2, 256, 333, 13, 8, 3, np.float16, 2),  # own layout; groups of 8 and 5 rows
 ]
