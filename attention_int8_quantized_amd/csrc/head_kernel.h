@@ -68,21 +68,10 @@ struct HeadArgs {
   float* top_prob;      // [n_rows] (may be null)
 };
 
-__device__ __forceinline__ float head_exp(float d) { return exp2f(d * kHeadLog2e); }
-
-// add logit x at index i (indices arrive in increasing order per lane)
-__device__ __forceinline__ void head_push(HeadState& st, float x, int i) {
-  if (x > st.m) {
-    st.s = st.s * head_exp(st.m - x) + 1.0f;  // m = -inf: s is 0 and stays 0
-    st.m = x;
-    st.idx = i;
-  } else if (x == st.m) {
-    if (st.idx == kHeadNone) st.idx = i;
-    if (x != -INFINITY) st.s += 1.0f;
-  } else if (x == x && x != -INFINITY) {
-    st.s += head_exp(x - st.m);
-  }
-}
+// exp(d) for d <= 0 on the hardware exponential (v_exp_f32, about 1 ulp); a
+// result below fp32's normal range reads as 0, which changes no sum here: every
+// sum holds a term exp(0) = 1.
+__device__ __forceinline__ float head_exp(float d) { return __builtin_amdgcn_exp2f(d * kHeadLog2e); }
 
 // symmetric in its arguments (so every lane of a butterfly gets the same bits)
 __device__ __forceinline__ HeadState head_merge(const HeadState& a, const HeadState& b) {
@@ -94,15 +83,39 @@ __device__ __forceinline__ HeadState head_merge(const HeadState& a, const HeadSt
   return r;
 }
 
+// The partner's state under a lane involution: DPP within rows of 16 lanes
+// (quad_perm [1,0,3,2] and [2,3,0,1], then the half-row and row mirrors), then
+// the gfx950 row swaps (lanes l ^ 16, l ^ 32), which hand each lane its own
+// value and its partner's in some order -- the merge is symmetric, so the order
+// does not matter.  After each step a lane and its partner hold the same bits,
+// so after the six steps every lane holds the wave's state.
+template <int CTRL>
+__device__ __forceinline__ HeadState head_dpp_merge(const HeadState& st) {
+  HeadState p;
+  p.m = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(st.m), CTRL, 0xF, 0xF, false));
+  p.s = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(st.s), CTRL, 0xF, 0xF, false));
+  p.idx = __builtin_amdgcn_update_dpp(0, st.idx, CTRL, 0xF, 0xF, false);
+  return head_merge(st, p);
+}
+
+template <bool ROW32>
+__device__ __forceinline__ HeadState head_swap_merge(const HeadState& st) {
+  const uint32_t m = __float_as_uint(st.m), s = __float_as_uint(st.s), i = (uint32_t)st.idx;
+  auto sm = ROW32 ? __builtin_amdgcn_permlane32_swap(m, m, false, false) : __builtin_amdgcn_permlane16_swap(m, m, false, false);
+  auto ss = ROW32 ? __builtin_amdgcn_permlane32_swap(s, s, false, false) : __builtin_amdgcn_permlane16_swap(s, s, false, false);
+  auto si = ROW32 ? __builtin_amdgcn_permlane32_swap(i, i, false, false) : __builtin_amdgcn_permlane16_swap(i, i, false, false);
+  const HeadState a = {__uint_as_float(sm[0]), __uint_as_float(ss[0]), (int)si[0], 0};
+  const HeadState b = {__uint_as_float(sm[1]), __uint_as_float(ss[1]), (int)si[1], 0};
+  return head_merge(a, b);
+}
+
 __device__ __forceinline__ HeadState head_wave_merge(HeadState st) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    HeadState p;
-    p.m = __shfl_xor(st.m, o, 64);
-    p.s = __shfl_xor(st.s, o, 64);
-    p.idx = __shfl_xor(st.idx, o, 64);
-    st = head_merge(st, p);
-  }
+  st = head_dpp_merge<0xB1>(st);   // quad_perm [1,0,3,2]: lane ^ 1
+  st = head_dpp_merge<0x4E>(st);   // quad_perm [2,3,0,1]: lane ^ 2
+  st = head_dpp_merge<0x141>(st);  // row_half_mirror: lane i <-> 7 - i of its 8
+  st = head_dpp_merge<0x140>(st);  // row_mirror: lane i <-> 15 - i of its 16
+  st = head_swap_merge<false>(st);
+  st = head_swap_merge<true>(st);
   return st;
 }
 
@@ -127,16 +140,18 @@ __device__ __forceinline__ HeadState head_state_of(const float (&x)[N], const in
   HeadState st = {-INFINITY, 0.0f, kHeadNone, 0};
 #pragma unroll
   for (int k = 0; k < N; ++k) {
-    // a NaN never compares; -inf is an ordinary value (first one wins)
-    if (x[k] > st.m || (x[k] == st.m && st.idx == kHeadNone)) {
-      st.idx = x[k] > st.m || st.idx == kHeadNone ? idx[k] : st.idx;
-      st.m = fmaxf(st.m, x[k]);
-    }
+    // a NaN never compares; -inf is an ordinary value (first one wins);
+    // selects rather than branches
+    const bool gt = x[k] > st.m;
+    const bool first = (x[k] == st.m) & (st.idx == kHeadNone);
+    st.idx = (gt | first) ? idx[k] : st.idx;
+    st.m = gt ? x[k] : st.m;
   }
   if (st.m != -INFINITY) {
     float e[N];
+    // exp(-inf - m) is 0; a NaN term is dropped
 #pragma unroll
-    for (int k = 0; k < N; ++k) e[k] = (x[k] == x[k] && x[k] != -INFINITY) ? head_exp(x[k] - st.m) : 0.0f;
+    for (int k = 0; k < N; ++k) e[k] = x[k] == x[k] ? head_exp(x[k] - st.m) : 0.0f;
     // pairwise, in a fixed order
 #pragma unroll
     for (int w = 1; w < N; w *= 2)
@@ -209,6 +224,10 @@ __global__ __launch_bounds__(kHeadThreads) void head_greedy_kernel(HeadArgs a) {
   if (!last) return;
 
   // the last block of the row: merge the row's block states in block order
+  // (a row of at most 64 blocks: wave 0 alone; merging with the empty state
+  // of an absent block leaves every bit unchanged, so both forms agree)
+  const bool one_wave = a.blocks_per_row <= 64;
+  if (one_wave && threadIdx.x >= 64) return;
   HeadState r = {-INFINITY, 0.0f, kHeadNone, 0};
   if ((int)threadIdx.x < a.blocks_per_row) {
     HeadSlot* p = slots + threadIdx.x;
@@ -226,8 +245,12 @@ __global__ __launch_bounds__(kHeadThreads) void head_greedy_kernel(HeadArgs a) {
     r.s = __uint_as_float((uint32_t)w[1]);
     r.idx = (int)(uint32_t)w[2];
   }
-  __syncthreads();  // lds is reused
-  r = head_block_merge(r, lds);
+  if (one_wave) {
+    r = head_wave_merge(r);
+  } else {
+    __syncthreads();  // lds is reused
+    r = head_block_merge(r, lds);
+  }
   if (threadIdx.x == 0) {
     a.token[row] = r.idx == kHeadNone ? -1 : r.idx;
     if (a.top_prob) a.top_prob[row] = r.m == -INFINITY ? NAN : 1.0f / r.s;
