@@ -1261,8 +1261,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_partials_kernel(const f
     const float2 m = part_ml[(size_t)s * n_pairs + pair];
     if (m.y > 0.0f) M = fmaxf(M, m.x);
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  M = wave_max_all(M);
   if (lane == 0) wmax[tid >> 6] = M;
   __syncthreads();
   M = wmax[0];
@@ -1275,7 +1274,9 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_partials_kernel(const f
 #pragma unroll
     for (int i = 0; i < B; ++i) {
       if (s0 + i * NSLOT < n_splits) {
-        const float w = (ml[i].y > 0.0f) ? exp2f(ml[i].x - M) : 0.0f;
+        // the hardware exponential: a weight below fp32's normal range reads
+        // as 0 beside the split at M, whose weight is 1
+        const float w = (ml[i].y > 0.0f) ? __builtin_amdgcn_exp2f(ml[i].x - M) : 0.0f;
         den = fmaf(w, ml[i].y, den);
         acc += w * o[i];
       }

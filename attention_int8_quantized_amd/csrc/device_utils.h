@@ -79,6 +79,17 @@ __device__ __forceinline__ float wave_max_groups(float x) {
   return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 
+// max over all 64 lanes: DPP within rows of 16 (lane ^ 1, lane ^ 2, the
+// half-row mirror i <-> 7 - i, the row mirror i <-> 15 - i), then the row
+// swaps of wave_max_groups; every lane returns the same value
+__device__ __forceinline__ float wave_max_all(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false)));
+  return wave_max_groups(x);
+}
+
 __device__ __forceinline__ float wave_sum_groups(float x) {
   x += __shfl_xor(x, 16, 64);
   x += __shfl_xor(x, 32, 64);
