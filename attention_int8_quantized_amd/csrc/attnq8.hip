@@ -110,15 +110,16 @@ int splits_for(int n_keys, int units, int hd) {
   return s;
 }
 
-// Default row group: as many rows of a KV head as fit 64 query vectors (four
-// vector tiles: the split-role instances).  The eight-tile instances hold up
-// to 128, but per call they measured slower at every head_dim than groups of
-// four tiles, which read the context twice as often: at 32 rows of 32 / 8
-// heads, 8,192 keys, 31.6 against 40.8 us at head_dim 128 and 24.5 against
-// 30.1 us at 64 (fp16 cache: 25.1 against 29.2 us).
+// Default row group: as many rows of a KV head as fit 128 query vectors at
+// head_dim 128 (eight vector tiles: the own layout's eight compute waves) and
+// 64 otherwise (four: the split-role instances).  Per call at 32 rows of 32 / 8
+// heads and 8,192 keys, head_dim 128: 22.3 us against 26.6 us for two groups
+// of four tiles (the general eight-tile instance took 33.7); at head_dim 64
+// the general eight-tile instance measured 30.1 against 24.5 us for four-tile
+// groups, which read the context twice as often (fp16 cache: 29.2 against
+// 25.1 us).
 int auto_rows_per_group(int G, int n_rows, int hd) {
-  (void)hd;
-  int rg = 64 / G;
+  int rg = (hd == 128 ? 128 : 64) / G;
   if (rg > n_rows) rg = n_rows;
   if (rg < 1) rg = 1;
   return rg;
@@ -149,18 +150,26 @@ KernelFn pick_nq(int nq) {
 // compute wave owns its vectors end to end.  (With two or three tiles over an
 // int8 cache that layout leaves the SIMDs' MFMA pipes to one wave each and
 // gains nothing over the split roles; those row groups keep the general body.)
-bool own_layout(bool kv16, int hd, int nq) { return hd == 256 && (nq == 6 || (kv16 && nq == 3)); }
-
-template <bool FINAL, bool QF32, bool KV16>
-KernelFn pick_own(int nq) {
-  if constexpr (KV16) return nq == 6 ? attend_own_f16kv_kernel<QF32, FINAL, 6> : attend_own_f16kv_kernel<QF32, FINAL, 3>;
-  else return nq == 6 ? attend_own_q8_kernel<QF32, FINAL, 6> : nullptr;
+// At head_dim 128 the eight-tile row groups take it too (eight compute waves
+// and their feeders).
+bool own_layout(bool kv16, int hd, int nq) {
+  return (hd == 256 && (nq == 6 || (kv16 && nq == 3))) || (hd == 128 && nq == 8);
 }
 
-// Threads per workgroup of the kernel pick_kernel returns (the own layout: eight waves).
+template <bool FINAL, bool QF32, bool KV16>
+KernelFn pick_own(int hd, int nq) {
+  if (hd == 128) {
+    if constexpr (KV16) return attend_own_f16kv_kernel<128, QF32, FINAL, 8>;
+    else return attend_own_q8_kernel<128, QF32, FINAL, 8>;
+  }
+  if constexpr (KV16) return nq == 6 ? attend_own_f16kv_kernel<256, QF32, FINAL, 6> : attend_own_f16kv_kernel<256, QF32, FINAL, 3>;
+  else return nq == 6 ? attend_own_q8_kernel<256, QF32, FINAL, 6> : nullptr;
+}
+
+// Threads per workgroup of the kernel pick_kernel returns.
 template <bool KV16>
 int threads_for(int hd, int nq) {
-  if (own_layout(KV16, hd, nq)) return 64 * kWaves;
+  if (own_layout(KV16, hd, nq)) return 64 * (hd == 128 ? own_waves<128, 8, KV16>() : kWaves);
   switch (hd) {
     case 256:
       switch (nq) {
@@ -174,7 +183,7 @@ int threads_for(int hd, int nq) {
 
 template <bool FINAL, bool KV16 = false>
 KernelFn pick_kernel(int hd, bool qf32, int nq) {
-  if (own_layout(KV16, hd, nq)) return qf32 ? pick_own<FINAL, true, KV16>(nq) : pick_own<FINAL, false, KV16>(nq);
+  if (own_layout(KV16, hd, nq)) return qf32 ? pick_own<FINAL, true, KV16>(hd, nq) : pick_own<FINAL, false, KV16>(hd, nq);
   switch (hd) {
     case 64: return qf32 ? pick_nq<64, true, FINAL, KV16>(nq) : pick_nq<64, false, FINAL, KV16>(nq);
     case 128: return qf32 ? pick_nq<128, true, FINAL, KV16>(nq) : pick_nq<128, false, FINAL, KV16>(nq);

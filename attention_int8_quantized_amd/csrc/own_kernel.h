@@ -45,21 +45,35 @@ namespace attnq8 {
 // four-wave TileCopier, share s going to feeder s % NF) and of the conversion
 // (K units u = F, F + NF, ... of the 16 (block u >> 1, 16-key subtile u & 1);
 // V blocks b = F, F + NF, ... of the 8).
-template <int NF, int F>
+template <int HD, int NF, int F>
 struct OwnFeeder {
-  static constexpr int HD = 256;
   using L = Stage<HD>;
   static constexpr int NB = L::NB;
+  static_assert(HD == 128 || HD == 256, "head_dim 128 or 256");
   static_assert(NF == 2 || NF >= 4, "the four copy shares split evenly");
   static constexpr int NSHARE = NF >= 4 ? (F < 4 ? 1 : 0) : 4 / NF;  // copy shares
   static constexpr int NKU = (2 * NB - F + NF - 1) / NF;     // K units
   static constexpr int NVB = (NB - F + NF - 1) / NF;         // V blocks
-  static constexpr int COPIES = 5 * NSHARE;                  // copies per tile (codes 2 x 2 + 1 scale per share)
+  // copies per tile: share s of a four-wave TileCopier issues 2 CPW code
+  // copies and, for s below its NS, one scale copy
+  static constexpr int copies_per_tile() {
+    using TC = TileCopier<L, 4>;
+    int n = 0;
+    for (int j = 0; j < NSHARE; ++j) n += 2 * TC::CPW + (F + NF * j < TC::NS ? 1 : 0);
+    return n;
+  }
+  static constexpr int COPIES = copies_per_tile();
+  // the K scale plane (64 NB bytes) goes in 256-byte parts to the first feeders
+  static constexpr int NKSP = NB / 4;
+  static constexpr int KSF = NF < NKSP ? NF : NKSP;
+  static constexpr int NKS = F < KSF ? (NKSP - F + KSF - 1) / KSF : 0;  // this feeder's parts
 
   TileCopier<L, 4> cp[NSHARE > 0 ? NSHARE : 1];
   int k_rd[NKU > 0 ? NKU : 1];        // K unit j: the lane's 8 codes within a stage
   int v_rd[NVB > 0 ? NVB : 1][2];     // V block j, dim tile dd: the lane's transposing read
   int vs_rd;                          // V scale rows of the lane's keys pi(h4, e)
+  // one key's NB V scales as NB / 2 dwords
+  typedef uint32_t srow_t __attribute__((ext_vector_type(NB / 2)));
 
   __device__ __forceinline__ void init(const AttendArgs& a, size_t head_rows, int k_end, int lane) {
 #pragma unroll
@@ -83,7 +97,7 @@ struct OwnFeeder {
 #pragma unroll
       for (int dd = 0; dd < 2; ++dd)
         v_rd[j][dd] = L::V_OFF + vkey * HD + 8 * (lane & 1) + 16 * chunk_slot<HD>(vkey, 2 * (F + NF * j) + dd);
-    vs_rd = L::VS_OFF + 64 * h4;
+    vs_rd = L::VS_OFF + 8 * NB * h4;  // key 4 h4 (a key row holds 2 NB bytes)
   }
 
   __device__ __forceinline__ void copy(uint32_t lds, int key0, bool live) const {
@@ -113,29 +127,23 @@ struct OwnFeeder {
 #pragma unroll
       for (int dd = 0; dd < 2; ++dd)
         vw[j][dd] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i32_t*)(st + v_rd[j][dd]));
-    u32x4_t srow[8];
+    srow_t srow[8];
     if constexpr (NVB > 0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) srow[e] = *(const u32x4_t*)(st + vs_rd + (e < 4 ? 16 * e : 256 + 16 * (e - 4)));
+      for (int e = 0; e < 8; ++e)
+        srow[e] = *(const srow_t*)(st + vs_rd + 2 * NB * (e < 4 ? e : 16 + (e - 4)));
     }
-    // the K scale plane (512 B) is copied by feeders 0 and 1 (or 0 alone)
-    constexpr int KS_PARTS = NF >= 2 ? 2 : 1;
-    uint32_t ksw[2];
-    if constexpr (F < KS_PARTS) {
+    uint32_t ksw[NKS > 0 ? NKS : 1];
 #pragma unroll
-      for (int i = 0; i < 2 / KS_PARTS; ++i)
-        ksw[i] = *(const uint32_t*)(st + L::KS_OFF + 256 * (F + i) + 4 * lane);
-    }
+    for (int i = 0; i < NKS; ++i) ksw[i] = *(const uint32_t*)(st + L::KS_OFF + 256 * (F + KSF * i) + 4 * lane);
 
 #pragma unroll
     for (int j = 0; j < NKU; ++j) {
       const int u = F + NF * j;
       *(half8_t*)(kf + (((u >> 1) * 2 + (u & 1)) * 64 + lane) * 16) = codes8_to_f16(kw[j].x, kw[j].y);
     }
-    if constexpr (F < KS_PARTS) {
 #pragma unroll
-      for (int i = 0; i < 2 / KS_PARTS; ++i) *(uint32_t*)(ksd + 256 * (F + i) + 4 * lane) = ksw[i];
-    }
+    for (int i = 0; i < NKS; ++i) *(uint32_t*)(ksd + 256 * (F + KSF * i) + 4 * lane) = ksw[i];
 #pragma unroll
     for (int j = 0; j < NVB; ++j) {
       const int b = F + NF * j;
@@ -164,11 +172,11 @@ struct OwnFeeder {
 // The feeders' loop: iteration t waits for this feeder's copies of tile t+1,
 // passes the barrier, copies tile t+3 into the stage of tile t and converts
 // tile t+1.  Iteration t_begin - 1 converts the first tile only.
-template <int NF, int F, int D, class Ring>
+template <int HD, int NF, int F, int D, class Ring>
 __device__ __forceinline__ void own_feed(const AttendArgs& a, size_t head_rows, int k_end, int t_begin, int t_end,
                                          int lane, Ring& r) {
-  using L = Stage<256>;
-  OwnFeeder<NF, F> fd;
+  using L = Stage<HD>;
+  OwnFeeder<HD, NF, F> fd;
   fd.init(a, head_rows, k_end, lane);
   fd.copy(r.ring0 + 0 * L::BYTES, t_begin * 32, t_begin < t_end);
   __builtin_amdgcn_sched_barrier(0);
@@ -196,10 +204,10 @@ __device__ __forceinline__ void own_feed(const AttendArgs& a, size_t head_rows, 
 // K and V^T fragments from the ring): iteration t waits for this feeder's
 // copies of tile t, passes the barrier and copies tile t+D-1 into the stage of
 // tile t-1.  Feeder F of NF takes code chunks F, F + NF, ... of each plane.
-template <int NF, int F, int D>
+template <int HD, int NF, int F, int D>
 __device__ __forceinline__ void own_feed16(const AttendArgs& a, size_t head_rows, int k_end, int t_begin, int t_end,
                                            int lane, uint32_t ring0) {
-  using L = Stage16<256>;
+  using L = Stage16<HD>;
   TileCopier<L, NF> cp;
   cp.kc = make_rsrc((const uint8_t*)a.kc + head_rows * L::ROW, k_end * L::ROW);
   cp.vc = make_rsrc((const uint8_t*)a.vc + head_rows * L::ROW, k_end * L::ROW);
@@ -220,13 +228,21 @@ __device__ __forceinline__ void own_feed16(const AttendArgs& a, size_t head_rows
   wait_vmcnt<0>();  // copies past the last tile may still be landing
 }
 
-template <bool QF32, bool FINAL, int NQ, bool KV16>
+// Feeding waves of an instance: at head_dim 256 the waves beyond the compute
+// waves of eight; at 128 (eight compute waves) four over an int8 cache, one
+// per copy share, and the two copying waves over an fp16 cache.
+template <int HD, int NQ, bool KV16>
+constexpr int own_feeders() { return HD == 256 ? kWaves - NQ : (KV16 ? 2 : 4); }
+template <int HD, int NQ, bool KV16>
+constexpr int own_waves() { return NQ + own_feeders<HD, NQ, KV16>(); }
+
+template <int HD, bool QF32, bool FINAL, int NQ, bool KV16>
 __device__ __forceinline__ void attend_own_body(const AttendArgs& a) {
-  constexpr int HD = 256;
+  static_assert((HD == 256 && NQ <= 6) || (HD == 128 && NQ == 8), "instances");
   using L = std::conditional_t<KV16, Stage16<HD>, Stage<HD>>;
   constexpr int NB = L::NB;                    // 32-dim blocks
   constexpr int NDT = HD / 16;                 // 16-dim output tiles
-  constexpr int NF = kWaves - NQ;              // feeding waves
+  constexpr int NF = own_feeders<HD, NQ, KV16>();  // feeding waves
   // ring stages: an int8 stage is free once converted (tiles t+1 .. t+3 in it);
   // an fp16 stage is read in place (tiles t .. t+3)
   constexpr int D = KV16 ? 4 : 3;
@@ -235,7 +251,7 @@ __device__ __forceinline__ void attend_own_body(const AttendArgs& a) {
   constexpr int KF_BYTES = KV16 ? 16 : NB * 2 * 1024;
   constexpr int VF_BYTES = KV16 ? 16 : NDT * 2 * 1024;
   constexpr int KS_BYTES = KV16 ? 16 : 32 * NB * 2;
-  static_assert(NQ >= 2 && NQ <= 6, "two to six compute waves");
+  static_assert(NQ >= 2 && NQ <= 8, "two to eight compute waves");
   static_assert(D * L::BYTES + 2 * (KF_BYTES + VF_BYTES + KS_BYTES) <= 160 * 1024, "LDS");
 
   struct Ring {
@@ -285,20 +301,20 @@ __device__ __forceinline__ void attend_own_body(const AttendArgs& a) {
     // compile-time)
     if constexpr (KV16) {
       // two waves copy; any others only keep the barriers
-      if (wave == NQ) own_feed16<2, 0, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_.ring0);
-      else if (wave == NQ + 1) own_feed16<2, 1, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_.ring0);
+      if (wave == NQ) own_feed16<HD, 2, 0, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_.ring0);
+      else if (wave == NQ + 1) own_feed16<HD, 2, 1, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_.ring0);
       else {
         __builtin_amdgcn_s_barrier();
         for (int t = t_begin; t < t_end; ++t) __syncthreads();
       }
     } else {
       switch (wave - NQ) {
-        case 0: own_feed<NF, 0, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
-        case 1: if constexpr (NF > 1) own_feed<NF, 1, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
-        case 2: if constexpr (NF > 2) own_feed<NF, 2, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
-        case 3: if constexpr (NF > 3) own_feed<NF, 3, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
-        case 4: if constexpr (NF > 4) own_feed<NF, 4, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
-        default: if constexpr (NF > 5) own_feed<NF, 5, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
+        case 0: own_feed<HD, NF, 0, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
+        case 1: if constexpr (NF > 1) own_feed<HD, NF, 1, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
+        case 2: if constexpr (NF > 2) own_feed<HD, NF, 2, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
+        case 3: if constexpr (NF > 3) own_feed<HD, NF, 3, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
+        case 4: if constexpr (NF > 4) own_feed<HD, NF, 4, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
+        default: if constexpr (NF > 5) own_feed<HD, NF, 5, D>(a, head_rows, k_end, t_begin, t_end, lane, rg_); break;
       }
     }
     return;
@@ -532,7 +548,7 @@ __device__ __forceinline__ void attend_own_body(const AttendArgs& a) {
     // a block with a shifted V fold (rare: a V scale above 512) takes this
     // tile's sum in units of 2^s: O *= 2^-s before its MFMAs, O *= 2^s after
     const uint2 shw = *(const uint2*)vshift[t & 1];
-    const bool shifted = (shw.x | shw.y) != 0;
+    const bool shifted = (shw.x | (NB > 4 ? shw.y : 0u)) != 0;  // bytes past NB are never written
     auto fold_scale = [&](int sign) {
 #pragma unroll
       for (int d = 0; d < NDT; ++d) {
@@ -599,15 +615,15 @@ __device__ __forceinline__ void attend_own_body(const AttendArgs& a) {
 #undef QR
 }
 
-template <bool QF32, bool FINAL, int NQ>
-__global__ __launch_bounds__(64 * kWaves) void attend_own_q8_kernel(const AttendArgs a) {
-  attend_own_body<QF32, FINAL, NQ, false>(a);
+template <int HD, bool QF32, bool FINAL, int NQ>
+__global__ __launch_bounds__((64 * own_waves<HD, NQ, false>())) void attend_own_q8_kernel(const AttendArgs a) {
+  attend_own_body<HD, QF32, FINAL, NQ, false>(a);
 }
 
 // The same layout over an fp16 K/V cache (no scales, no conversion).
-template <bool QF32, bool FINAL, int NQ>
-__global__ __launch_bounds__(64 * kWaves) void attend_own_f16kv_kernel(const AttendArgs a) {
-  attend_own_body<QF32, FINAL, NQ, true>(a);
+template <int HD, bool QF32, bool FINAL, int NQ>
+__global__ __launch_bounds__((64 * own_waves<HD, NQ, true>())) void attend_own_f16kv_kernel(const AttendArgs a) {
+  attend_own_body<HD, QF32, FINAL, NQ, true>(a);
 }
 
 }  // namespace attnq8
