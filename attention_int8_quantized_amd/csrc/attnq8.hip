@@ -110,16 +110,17 @@ int splits_for(int n_keys, int units, int hd) {
   return s;
 }
 
-// Default row group: as many rows of a KV head as fit 128 query vectors at
-// head_dim 128 (eight vector tiles: the own layout's eight compute waves) and
-// 64 otherwise (four: the split-role instances).  Per call at 32 rows of 32 / 8
-// heads and 8,192 keys, head_dim 128: 22.3 us against 26.6 us for two groups
-// of four tiles (the general eight-tile instance took 33.7); at head_dim 64
-// the general eight-tile instance measured 30.1 against 24.5 us for four-tile
-// groups, which read the context twice as often (fp16 cache: 29.2 against
-// 25.1 us).
+// Default row group: as many rows of a KV head as fit 64 query vectors (four
+// vector tiles: the split-role instances).  Groups of up to 128 read the
+// context half as often but write twice the split partials: at 32 rows of
+// 32 / 8 heads and 8,192 keys, head_dim 128, one group of 128 vectors (the own
+// layout) takes 25.0 against 25.6 us for the attention kernel and 31.9 against
+// 30.5 us for the call with the reducer; at head_dim 64 the general
+// eight-tile instance measured 30.1 against 24.5 us per call (fp16 cache: 29.2
+// against 25.1 us).
 int auto_rows_per_group(int G, int n_rows, int hd) {
-  int rg = (hd == 128 ? 128 : 64) / G;
+  (void)hd;
+  int rg = 64 / G;
   if (rg > n_rows) rg = n_rows;
   if (rg < 1) rg = 1;
   return rg;

@@ -1,15 +1,16 @@
-// Attention at head_dim 256 in a layout in which each compute wave owns 16
-// query vectors end to end.  The library launches it for row groups of six
+// Attention in a layout in which each compute wave owns 16 query vectors end
+// to end.  The library launches it at head_dim 256 for row groups of six
 // vector tiles (such as the prompt chunk's 8 queries x 12 heads) over an int8
 // or fp16 cache, and over an fp16 cache also for three (the verify window's
-// 8 rows x 6 heads); the body takes two to six compute waves.
+// 8 rows x 6 heads); at head_dim 128 for row groups of five to eight vector
+// tiles (such as the verify batch's 32 rows x 4 heads) over either cache.
 //
 // Waves 0..NQ-1 each own one vector tile: per 32-key tile they compute
 // S^T = K Q^T, the mask and the online softmax, and then O^T += V^T P^T over all
-// sixteen 16-dim tiles of the output with p straight from their own registers
-// (no hand-off of p through LDS and no second barrier per tile).  The other
-// 8 - NQ waves feed them: they issue the direct-to-LDS copies of the int8 tiles
-// and, one tile ahead, convert K to fp16 fragments and V to exact fp16 hi + lo
+// 16-dim tiles of the output with p straight from their own registers (no
+// hand-off of p through LDS and no second barrier per tile).  The other waves
+// feed them: they issue the direct-to-LDS copies of the int8 tiles and, one
+// tile ahead, convert K to fp16 fragments and V to exact fp16 hi + lo
 // fragments (dV * code, with the general body's power-of-two shift for a block
 // holding a V scale above 512) in LDS, where every compute wave reads them.  The
 // arithmetic of each output element is the same as in the general attention
@@ -17,17 +18,21 @@
 // terms in the same order, same reference-point policy), so the two produce
 // identical results.
 //
-// With six tiles, SIMDs 0 and 1 carry two compute waves each and SIMDs 2 and 3
-// one compute wave and one feeding wave; with three, SIMDs 0..2 carry one
-// compute wave and one other wave each and SIMD 3 two other waves (over an fp16
-// cache two of the five copy and three only keep the barriers).
+// Head_dim 256 (eight waves): with six tiles, SIMDs 0 and 1 carry two compute
+// waves each and SIMDs 2 and 3 one compute wave and one feeding wave; with
+// three, SIMDs 0..2 carry one compute wave and one other wave each and SIMD 3
+// two other waves (over an fp16 cache two of the five copy and three only keep
+// the barriers).  Head_dim 128: eight compute waves (two per SIMD) and four
+// feeders, one per SIMD (int8 cache: each a quarter of the copies and of the
+// conversion), or two copying feeders (fp16 cache).
 //
-// LDS: a ring of three int8 stages (a stage is free once its tile has been
-// converted), double-buffered K fragments (16 KB), K scales (512 B) and V^T
-// fragments (32 KB), and per tile a byte per block that carries the V fold's
-// shift (0 unless the block holds a V scale above 512): 151,568 B in all.  Over an fp16 cache nothing is
-// converted: the compute waves read K and V^T fragments from a ring of four
-// 32 KB stages, and the two feeders only copy.
+// LDS at head_dim 256: a ring of three int8 stages (a stage is free once its
+// tile has been converted), double-buffered K fragments (16 KB), K scales
+// (512 B) and V^T fragments (32 KB), and per tile a byte per block that carries
+// the V fold's shift (0 unless the block holds a V scale above 512): 151,568 B
+// in all (75,792 B at head_dim 128).  Over an fp16 cache nothing is converted:
+// the compute waves read K and V^T fragments from a ring of four stages (32 KB
+// each at head_dim 256, 16 KB at 128), and the feeders only copy.
 //
 // Per iteration t (one workgroup barrier each): the copying feeders have waited
 // for their copies of tile t+1; after the barrier they copy tile t+3 into the

@@ -7,7 +7,8 @@ long-context verify workload (24 Q / 4 KV heads, head_dim 256, context 131,072,
 32,768-token int8 context, 2,048 causal queries).  The headline `value` is the
 verify call's KV GB/s; the prompt's TFLOP/s is reported beside it.  The other
 verify configurations (the verify window, the verify batch with the pages' R4
-row groups and with the library's own grouping, the tiny verify) are timed in
+row groups, with the library's own grouping and as one group of all 32 rows,
+the tiny verify) are timed in
 the same run and reported in `verify_configs`.
 
 Inputs are seeded synthetic data resident in HBM before timing, each workload
@@ -478,7 +479,8 @@ def issued_mfma_flops(w, path):
 # The verify configurations reported beside the headline: (workload, rows_per_group,
 # label); rows_per_group 0 = the library's own grouping.
 EXTRA_VERIFY = [("verify_window", 0, "verify_window"), ("verify_batch", 4, "verify_batch_r4"),
-                ("verify_batch", 0, "verify_batch_auto"), ("tiny_verify", 0, "tiny_verify")]
+                ("verify_batch", 0, "verify_batch_auto"), ("verify_batch", 32, "verify_batch_r32"),
+                ("tiny_verify", 0, "tiny_verify")]
 
 
 def time_verify_configs(ops, dev, args, steps, hold):

@@ -68,8 +68,7 @@ enum { ATTNQ8_F32 = 0, ATTNQ8_F16 = 1 };
  * group that reads one KV head -- rows_per_group * n_q_heads / n_kv_heads
  * query vectors, at most 128 -- and splits the group's visible context into
  * n_splits ranges of whole 32-key tiles.  rows_per_group = 0 picks the largest
- * group of at most 128 query vectors at head_dim 128 and 64 otherwise (at
- * least one row); n_splits = 0 picks
+ * group of at most 64 query vectors (at least one row); n_splits = 0 picks
  * attn_verify_q8_splits().  The grouping and split count change only the
  * rounding of the result.
  *

@@ -44,7 +44,8 @@ def test_auto_splits(lib):
     assert f(24, 4, 256, 20676, 8, 0) == 64
     assert f(24, 4, 256, 131072, 4, 0) == 64
     assert f(24, 4, 256, 20676, 32, 0) == 16     # at 256, 10 rows (60 vectors) per group: 4 groups
-    assert f(32, 8, 128, 8192, 32, 0) == 32      # one group of 128 vectors per KV head
+    assert f(32, 8, 128, 8192, 32, 0) == 16      # two groups of 64 vectors per KV head
+    assert f(32, 8, 128, 8192, 32, 32) == 32     # one group of 128 vectors per KV head
     assert f(32, 8, 128, 8192, 32, 4) == 4
     assert f(4, 1, 64, 256, 4, 0) == 4         # 260 keys -> 9 tiles -> at most 4 splits
     assert f(4, 1, 64, 0, 1, 0) == 1

@@ -18,7 +18,8 @@ def _dev(inp):
 
 
 @pytest.mark.parametrize("name,rg", [("tiny_verify", 0), ("verify_window", 0), ("verify_window", 1),
-                                     ("verify_batch", 4), ("verify_batch", 0), ("long_verify", 0)])
+                                     ("verify_batch", 4), ("verify_batch", 0), ("verify_batch", 32),
+                                     ("long_verify", 0)])
 def test_verify_f16kv_workloads(name, rg):
     w = W.WORKLOADS[name]
     note(f"verify fp16 cache {name} rows_per_group={rg}")
@@ -38,8 +39,8 @@ SMALL = [
     (12, 1, 256, 100, 8, 0, 0, np.float32, 17),
     (32, 8, 128, 500, 32, 1, 5, np.float32, 0),
     (16, 2, 64, 1000, 9, 0, 0, np.float16, 0),
-    (64, 1, 128, 70, 2, 0, 0, np.float32, 0),   # automatic: two rows (128 vectors) per group
-    (64, 1, 128, 70, 2, 1, 0, np.float32, 0),   # one row (64 vectors) per group
+    (64, 1, 128, 70, 2, 0, 0, np.float32, 0),   # automatic: one row (64 vectors) per group
+    (64, 1, 128, 70, 2, 2, 0, np.float32, 0),   # 128 vectors in one group: the own layout
     (24, 4, 256, 2000, 8, 0, 63, np.float32, 0),
     (48, 1, 256, 300, 2, 2, 0, np.float16, 5),  # 96 vectors: the largest group at hd 256
     (24, 2, 256, 400, 8, 8, 0, np.float32, 0),   # 96 vectors per group: the own layout

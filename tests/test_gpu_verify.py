@@ -48,6 +48,7 @@ def test_i8_to_f16_all_byte_pairs():
     ("verify_batch", 4),
     ("verify_batch", 1),
     ("verify_batch", 0),
+    ("verify_batch", 32),
     ("long_verify", 0),
 ])
 def test_workload_parity(name, rg):
@@ -66,14 +67,14 @@ SMALL = [
     (8, 8, 64, 31, 5, 2, 1, np.float32, 3),
     (6, 2, 128, 33, 7, 3, 2, np.float16, 0),
     (12, 1, 256, 100, 8, 0, 0, np.float32, 17),
-    (32, 8, 128, 500, 32, 0, 0, np.float32, 0),   # automatic: one group of 128 vectors (own layout)
-    (32, 8, 128, 500, 32, 16, 0, np.float32, 0),  # two groups of 16 rows (64 vectors)
+    (32, 8, 128, 500, 32, 0, 0, np.float32, 0),   # automatic: two groups of 16 rows (64 vectors)
+    (32, 8, 128, 500, 32, 32, 0, np.float32, 0),  # one group of 128 vectors: the own layout
     (32, 8, 128, 500, 32, 20, 3, np.float16, 3),  # own layout; groups of 20 and 12 rows (80, 48 vectors)
     (32, 8, 128, 500, 32, 1, 5, np.float32, 0),
     (16, 2, 64, 1000, 9, 0, 0, np.float16, 0),
     (3, 1, 256, 64, 3, 0, 3, np.float32, 0),
-    (64, 1, 128, 70, 2, 0, 0, np.float32, 0),   # automatic: two rows (128 vectors) in one group
-    (64, 1, 128, 70, 2, 1, 0, np.float32, 0),   # one row (64 vectors) per group
+    (64, 1, 128, 70, 2, 0, 0, np.float32, 0),   # automatic: one row (64 vectors) per group
+    (64, 1, 128, 70, 2, 2, 0, np.float32, 0),   # 128 query vectors in one group: the own layout
     (128, 1, 64, 45, 1, 0, 0, np.float32, 1),   # 8 waves, one row
     (24, 4, 256, 2000, 8, 0, 63, np.float32, 0),  # every split 1 tile
     (24, 4, 256, 777, 32, 0, 0, np.float32, 5),   # 32 rows: groups of 10, 10, 10, 2
