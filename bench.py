@@ -16,7 +16,8 @@ in rotating copies of at least 1 GB (four times the 256 MB Infinity Cache)
 so that repeats come from HBM.  Durations come from HIP events recorded on the
 library's stream: around each whole verify call (attention kernel + reducer,
 nothing recorded between them) and each prompt call, and on alternate steps one
-more event after the attention kernel, which times it alone in the call.  The
+more event after the attention kernel, which times it and the reducer after it
+(with that launch's dispatch gap) separately.  The
 verify roofline's launch duration comes from a region of the attention kernel
 alone launched back to back after the steps (events around the region divided
 by its launches), so that no per-launch event latency enters it.
@@ -241,8 +242,8 @@ def main():
     t_start.record()
     # Events bracket the verify call (kernel + reducer) and the prompt call of
     # every step; on odd steps one more event between the attention kernel and
-    # the reducer times the kernel alone (its roofline).  The call's time is
-    # taken from the even steps, which have nothing recorded inside the call.
+    # the reducer times the kernel and the reducer separately.  The call's time
+    # is taken from the even steps, which have nothing recorded inside the call.
     for i in range(K):
         e = ev[i]
         e[0].record()
@@ -276,6 +277,7 @@ def main():
     odd = [i for i in range(K) if i % 2 == 1 or K < 2]
     even = [i for i in range(K) if i % 2 == 0]
     k1 = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in odd]) * 1e-3  # s
+    kr = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in odd]) * 1e-3  # the reducer after it
     kv = np.array([ev[i][0].elapsed_time(ev[i][2]) for i in even]) * 1e-3
     kp = np.array([ev[i][2].elapsed_time(ev[i][3]) for i in range(K)]) * 1e-3
     step_ms = t_start.elapsed_time(t_end) / K
@@ -312,7 +314,7 @@ def main():
         "verify": {
             "us_per_call": round(verify_s * 1e6, 3),
             "kernel_us": round(k1_mean * 1e6, 3),
-            "reduce_us": round((verify_s - k1_mean) * 1e6, 3),
+            "reduce_us": round(float(np.mean(kr)) * 1e6, 3),
             "kv_bytes": vbytes,
             "unique_kv_bytes": wv.unique_kv_bytes(),
             "partial_bytes": ops.workspace_bytes(wv.n_rows, wv.n_q_heads, wv.head_dim, S),
@@ -502,11 +504,10 @@ def time_verify_configs(ops, dev, args, steps, hold):
             cache[name] = rotating_copies([inp.q, inp.k_codes, inp.k_scales, inp.v_codes, inp.v_scales],
                                           dev, args.rotate_bytes)
         bufs = cache[name]
-        k1, k2, S, path = time_verify(ops, bufs, w, rg, steps, args.warmup, hold)
+        k1, k2, tot, S, path = time_verify(ops, bufs, w, rg, steps, args.warmup, hold)
         rg_used = rows_per_group_of(path, rg or w.rows_per_group)
         per_pass = w.visible_kv_bytes(rg_used)
         uniq = w.unique_kv_bytes()
-        tot = k1 + k2
         out[label] = {
             "workload": name,
             "rows_per_group": rg_used,
@@ -949,8 +950,10 @@ SWEEP_GROUPS = (1, 4, 8)
 
 
 def time_verify(ops, bufs, w, rows_per_group, steps, warmup, hold):
-    """Mean durations (s) over rotating inputs: the attention kernel alone, and the
-    rest of the verify call (reducer and the launch gap before it)."""
+    """Mean durations (s) over rotating inputs: the attention kernel alone and the
+    reducer after it (with the launch gap before it), both from the steps that
+    record an event between the two, and the whole call from the steps that
+    do not."""
     import torch
 
     S = ops.verify_splits(w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx_len, w.n_rows,
@@ -983,8 +986,9 @@ def time_verify(ops, bufs, w, rows_per_group, steps, warmup, hold):
     odd = [e for i, e in enumerate(ev) if i % 2 == 1 or steps < 2]
     even = [e for i, e in enumerate(ev) if i % 2 == 0]
     k1 = float(np.mean([e[0].elapsed_time(e[1]) for e in odd])) * 1e-3
-    k2 = float(np.mean([e[0].elapsed_time(e[2]) for e in even])) * 1e-3 - k1
-    return k1, k2, S, path
+    call = float(np.mean([e[0].elapsed_time(e[2]) for e in even])) * 1e-3
+    k2 = float(np.mean([e[1].elapsed_time(e[2]) for e in odd])) * 1e-3
+    return k1, k2, call, S, path
 
 
 def sweep(args):
@@ -1008,12 +1012,10 @@ def sweep(args):
         torch.cuda.synchronize()
         cells = {}
         for rg in SWEEP_GROUPS:
-            k1, k2, S, path = time_verify(ops, bufs, w, rg, steps, args.warmup, hold)
-            cells[rg] = (k1, k2, S, path)
-        t1 = cells[1][0] + cells[1][1]
+            cells[rg] = time_verify(ops, bufs, w, rg, steps, args.warmup, hold)
+        t1 = cells[1][2]
         for rg in SWEEP_GROUPS:
-            k1, k2, S, path = cells[rg]
-            tot = k1 + k2
+            k1, k2, tot, S, path = cells[rg]
             line = {
                 "mode": "sweep", "n_q_heads": hq, "n_kv_heads": hkv, "head_dim": hd,
                 "ctx": ctx, "rows": SWEEP_ROWS, "rows_per_group": rg, "splits": S,
