@@ -17,11 +17,13 @@ so that repeats come from HBM.  Durations come from HIP events recorded on the
 library's stream: around each whole verify call (attention kernel + reducer,
 nothing recorded between them) and each prompt call, and on alternate steps one
 more event after the attention kernel, which times it and the reducer after it
-(with that launch's dispatch gap) separately.  The
-verify roofline's launch duration comes from a region of the attention kernel
-alone launched back to back after the steps (events around the region divided
-by its launches), so that no per-launch event latency enters it.
-The GPU is held by a spin kernel while the timed launches are queued so that
+(with that launch's dispatch gap) separately.  An event
+between two launches adds several microseconds of its own, so the attention
+kernel and the reducer are also timed each alone, launched back to back after
+the steps (events around the region divided by its launches: the GPU time per
+launch with its dispatch gap and no per-launch event latency); the verify
+roofline's launch duration is the attention kernel's.
+The GPU is kept busy by plain read kernels while the timed launches are queued so that
 host submission latency does not enter them.  The practical HBM read ceiling
 (a plain 1 GiB read by the library's attnq8_stream_read) is reported beside the
 8 TB/s peak.
@@ -273,6 +275,14 @@ def main():
     r1.record()
     torch.cuda.synchronize()
     kr_mean = r0.elapsed_time(r1) / KR * 1e-3  # s
+    # the reducer alone, the same way (its partials stay those of the last call)
+    hold(60e-6 * KR + 1e-3)
+    r0.record()
+    for i in range(KR):
+        reduce_call()
+    r1.record()
+    torch.cuda.synchronize()
+    rr_mean = r0.elapsed_time(r1) / KR * 1e-3  # s
 
     odd = [i for i in range(K) if i % 2 == 1 or K < 2]
     even = [i for i in range(K) if i % 2 == 0]
@@ -323,6 +333,7 @@ def main():
             "kernel_gbs": round(k1_gbs, 2),
             "kernel_frac_hbm": round(k1_gbs / HBM_PEAK_GBS, 4),
             "kernel_us_back_to_back": round(kr_mean * 1e6, 3),
+            "reduce_us_back_to_back": round(rr_mean * 1e6, 3),
             "launches_back_to_back": KR,
         },
         "roofline": {
@@ -504,7 +515,7 @@ def time_verify_configs(ops, dev, args, steps, hold):
             cache[name] = rotating_copies([inp.q, inp.k_codes, inp.k_scales, inp.v_codes, inp.v_scales],
                                           dev, args.rotate_bytes)
         bufs = cache[name]
-        k1, k2, tot, S, path = time_verify(ops, bufs, w, rg, steps, args.warmup, hold)
+        k1, k2, tot, S, path, kb, rb = time_verify(ops, bufs, w, rg, steps, args.warmup, hold)
         rg_used = rows_per_group_of(path, rg or w.rows_per_group)
         per_pass = w.visible_kv_bytes(rg_used)
         uniq = w.unique_kv_bytes()
@@ -517,6 +528,8 @@ def time_verify_configs(ops, dev, args, steps, hold):
             "us_per_call": round(tot * 1e6, 3),
             "kernel_us": round(k1 * 1e6, 3),
             "reduce_us": round(k2 * 1e6, 3),
+            "kernel_us_back_to_back": round(kb * 1e6, 3),
+            "reduce_us_back_to_back": round(rb * 1e6, 3),
             "kv_bytes_per_pass": per_pass,
             "unique_kv_bytes": uniq,
             "partial_bytes": ops.workspace_bytes(w.n_rows, w.n_q_heads, w.head_dim, S),
@@ -952,8 +965,8 @@ SWEEP_GROUPS = (1, 4, 8)
 def time_verify(ops, bufs, w, rows_per_group, steps, warmup, hold):
     """Mean durations (s) over rotating inputs: the attention kernel alone and the
     reducer after it (with the launch gap before it), both from the steps that
-    record an event between the two, and the whole call from the steps that
-    do not."""
+    record an event between the two, the whole call from the steps that do
+    not, and each kernel launched back to back (per launch)."""
     import torch
 
     S = ops.verify_splits(w.n_q_heads, w.n_kv_heads, w.head_dim, w.ctx_len, w.n_rows,
@@ -988,7 +1001,25 @@ def time_verify(ops, bufs, w, rows_per_group, steps, warmup, hold):
     k1 = float(np.mean([e[0].elapsed_time(e[1]) for e in odd])) * 1e-3
     call = float(np.mean([e[0].elapsed_time(e[2]) for e in even])) * 1e-3
     k2 = float(np.mean([e[1].elapsed_time(e[2]) for e in odd])) * 1e-3
-    return k1, k2, call, S, path
+    # each kernel alone, launched back to back (events around the region)
+    R = max(steps, 10)
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    regions = []
+    for part in ("kernel", "reduce"):
+        torch.cuda.synchronize()
+        hold(60e-6 * R + 1e-3)
+        r0.record()
+        for i in range(R):
+            if part == "kernel":
+                q, kc, ks, vc, vs = bufs[(i + 1) % len(bufs)]
+                ops.verify_partials(q, kc, ks, vc, vs, ctx_len=w.ctx_len,
+                                    rows_per_group=rows_per_group, n_splits=S, workspace=ws)
+            else:
+                ops.reduce_partials(ws, w.n_rows, w.n_q_heads, w.head_dim, S, out=out)
+        r1.record()
+        torch.cuda.synchronize()
+        regions.append(r0.elapsed_time(r1) / R * 1e-3)
+    return k1, k2, call, S, path, regions[0], regions[1]
 
 
 def sweep(args):
@@ -1015,7 +1046,7 @@ def sweep(args):
             cells[rg] = time_verify(ops, bufs, w, rg, steps, args.warmup, hold)
         t1 = cells[1][2]
         for rg in SWEEP_GROUPS:
-            k1, k2, tot, S, path = cells[rg]
+            k1, k2, tot, S, path = cells[rg][:5]
             line = {
                 "mode": "sweep", "n_q_heads": hq, "n_kv_heads": hkv, "head_dim": hd,
                 "ctx": ctx, "rows": SWEEP_ROWS, "rows_per_group": rg, "splits": S,
