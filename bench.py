@@ -283,6 +283,15 @@ def main():
     r1.record()
     torch.cuda.synchronize()
     rr_mean = r0.elapsed_time(r1) / KR * 1e-3  # s
+    # and whole calls back to back (attention kernel + reducer, no event inside)
+    hold(60e-6 * KR + 1e-3)
+    r0.record()
+    for i in range(KR):
+        verify_call(i + 1)
+        reduce_call()
+    r1.record()
+    torch.cuda.synchronize()
+    cr_mean = r0.elapsed_time(r1) / KR * 1e-3  # s
 
     odd = [i for i in range(K) if i % 2 == 1 or K < 2]
     even = [i for i in range(K) if i % 2 == 0]
@@ -334,6 +343,7 @@ def main():
             "kernel_frac_hbm": round(k1_gbs / HBM_PEAK_GBS, 4),
             "kernel_us_back_to_back": round(kr_mean * 1e6, 3),
             "reduce_us_back_to_back": round(rr_mean * 1e6, 3),
+            "call_us_back_to_back": round(cr_mean * 1e6, 3),
             "launches_back_to_back": KR,
         },
         "roofline": {
