@@ -261,37 +261,27 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
 
-    # The attention kernel alone, launched back to back over the rotating
-    # inputs after the steps: events around the whole region, divided by the
-    # launches in it, give the launch duration of the roofline (a kernel
-    # bracketed by its own events also carries the dispatch latency).
+    # Back-to-back regions after the steps (events around each region, divided
+    # by its launches; a kernel bracketed by its own events also carries the
+    # event's latency): whole calls (attention kernel + reducer, no event
+    # inside), the reducer alone, and last the attention kernel alone over the
+    # rotating inputs, whose launch duration is the roofline's.
     KR = max(K, 10)
-    torch.cuda.synchronize()
-    hold(60e-6 * KR + 1e-3)
     r0, r1 = E(), E()
-    r0.record()
-    for i in range(KR):
-        verify_call(i + 1)
-    r1.record()
-    torch.cuda.synchronize()
-    kr_mean = r0.elapsed_time(r1) / KR * 1e-3  # s
-    # the reducer alone, the same way (its partials stay those of the last call)
-    hold(60e-6 * KR + 1e-3)
-    r0.record()
-    for i in range(KR):
-        reduce_call()
-    r1.record()
-    torch.cuda.synchronize()
-    rr_mean = r0.elapsed_time(r1) / KR * 1e-3  # s
-    # and whole calls back to back (attention kernel + reducer, no event inside)
-    hold(60e-6 * KR + 1e-3)
-    r0.record()
-    for i in range(KR):
-        verify_call(i + 1)
-        reduce_call()
-    r1.record()
-    torch.cuda.synchronize()
-    cr_mean = r0.elapsed_time(r1) / KR * 1e-3  # s
+
+    def region(body):
+        torch.cuda.synchronize()
+        hold(60e-6 * KR + 1e-3)
+        r0.record()
+        for i in range(KR):
+            body(i + 1)
+        r1.record()
+        torch.cuda.synchronize()
+        return r0.elapsed_time(r1) / KR * 1e-3  # s
+
+    cr_mean = region(lambda i: (verify_call(i), reduce_call()))
+    rr_mean = region(lambda i: reduce_call())  # (the partials of the last call)
+    kr_mean = region(verify_call)
 
     odd = [i for i in range(K) if i % 2 == 1 or K < 2]
     even = [i for i in range(K) if i % 2 == 0]
