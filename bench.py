@@ -459,7 +459,7 @@ def kernel_of_path(path):
     b = lambda x: "true" if x else "false"  # noqa: E731
     if " own" in path:
         name = "attend_own_f16kv_kernel" if kv16 else "attend_own_q8_kernel"
-        return f"{name}<{b(qf32)}, {b(final)}, {nq}>"
+        return f"{name}<{hd}, {b(qf32)}, {b(final)}, {nq}>"
     name = "attend_f16kv_kernel" if kv16 else "attend_q8_kernel"
     return f"{name}<{hd}, {b(qf32)}, {b(final)}, {nq}>"
 
@@ -618,12 +618,12 @@ def summarize_pmc(paths):
 TRAFFIC_KEYS = {
     "verify": "attend_q8_kernel<256, true, false, 2>",
     "verify_window": "attend_q8_kernel<256, true, false, 3>",
-    "prompt": "attend_own_q8_kernel<false, true, 6>",
+    "prompt": "attend_own_q8_kernel<256, false, true, 6>",
     "reduce": "reduce_partials_kernel<256>",
     "append": "kv_append_q8_kernel<true>",
     "head": "head_greedy_kernel",
     "verify_f16kv": "attend_f16kv_kernel<256, true, false, 2>",
-    "prompt_f16kv": "attend_own_f16kv_kernel<false, true, 6>",
+    "prompt_f16kv": "attend_own_f16kv_kernel<256, false, true, 6>",
 }
 
 

@@ -38,7 +38,9 @@ def test_issued_mfma_flops_and_kernel_names():
     import workloads as W
 
     p = "prompt kvq8 hd256 qf16 tiles6 own rows_per_group8 groups256 kv_heads1"
-    assert bench.kernel_of_path(p) == "attend_own_q8_kernel<false, true, 6>"
+    assert bench.kernel_of_path(p) == "attend_own_q8_kernel<256, false, true, 6>"
+    o = "verify kvq8 hd128 qf32 tiles8 own rows_per_group32 groups1 splits32 kv_heads8"
+    assert bench.kernel_of_path(o) == "attend_own_q8_kernel<128, true, false, 8>"
     # fp16 q: 16 QK + 48 PV MFMAs per (16 vectors, 32 keys) = 2,048 FLOP per pair,
     # twice the algorithmic 4 * 256 = 1,024, plus the masked halves of diagonal tiles
     r = bench.issued_mfma_flops(W.PROMPT_CHUNK, p) / W.PROMPT_CHUNK.algorithmic_flops()
