@@ -105,9 +105,11 @@ def test_f16kv_group_limit_at_256():
     (96, 8, 256, 400, 229, None, np.float16),   # 8 rows x 12 heads; last group 5 rows
     (11, 1, 256, 1900, 1800, None, np.float32),  # 8 rows x 11 heads = 88 vectors
     (32, 2, 256, 800, 700, 3, np.float16),       # 6 rows x 16 heads; context past the chunk
+    (32, 2, 128, 900, 800, None, np.float16),    # head_dim 128: 7 rows x 16 heads = 112 vectors
+    (64, 1, 128, 700, 600, 0, np.float32),       # 2 rows x 64 heads = 128 vectors
 ])
 def test_prompt_f16kv_own_layout(hq, hkv, hd, kv_len, n, pos0, qd):
-    """Row groups of six vector tiles at head_dim 256 take the own layout."""
+    """Row groups of six vector tiles at head_dim 256, five to eight at 128, take the own layout."""
     w = W.PromptWorkload("p16own", hq, hkv, hd, kv_len, n, seed=kv_len + 3 * n, q_pos0=pos0)
     note(f"prompt fp16 cache own layout {hq}/{hkv} hd{hd} kv{kv_len} n{n} {qd.__name__}")
     inp = W.generate_f16kv(w)
@@ -116,7 +118,7 @@ def test_prompt_f16kv_own_layout(hq, hkv, hd, kv_len, n, pos0, qd):
     got = ops.prompt_f16kv(q, k, v, q_pos0=w.pos0, kv_len=w.kv_len).cpu().numpy()
     path = ops.last_path()
     note(f"  path: {path}")
-    assert "tiles6 own" in path
+    assert ("tiles6 own" if hd == 256 else "tiles8 own") in path
     rows = sorted(set(list(range(0, 18)) + list(range(n - 18, n)) +
                       list(np.random.default_rng(n).integers(0, n, 24))))
     ref = oracle.prompt_f16kv(inp.q, inp.k, inp.v, w.pos0, rows=rows)

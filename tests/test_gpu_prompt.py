@@ -91,6 +91,10 @@ OWN = [
     (32, 2, 256, 800, 700, None, 0, np.float16),    # 6 rows x 16 heads; last group 4 rows
     (11, 1, 256, 1900, 1800, None, 0, np.float32),  # 8 rows x 11 heads = 88 vectors
     (12, 1, 256, 1900, 1795, 17, 0, np.float16),    # last group 3 rows; context past the chunk
+    # head_dim 128: eight compute waves for row groups of 65..128 vectors
+    (32, 2, 128, 900, 800, None, 0, np.float16),    # 7 rows x 16 heads = 112 vectors
+    (64, 1, 128, 700, 600, 0, 3, np.float32),       # 2 rows x 64 heads = 128 vectors, fp32 q
+    (16, 1, 128, 1500, 1400, 31, 0, np.float16),    # 6 rows x 16 heads; context past the chunk
 ]
 
 
@@ -104,7 +108,7 @@ def test_own_layout_shapes(case):
     inp.q = inp.q.astype(qd)
     _, got, path = run_prompt(w, inp)
     note(f"  path: {path}")
-    assert "tiles6 own" in path
+    assert ("tiles6 own" if hd == 256 else "tiles8 own") in path
     # the first and last rows of every row group near the ends, a spread in between
     rows = sorted(set(list(range(0, 18)) + list(range(n - 18, n)) +
                       list(np.random.default_rng(n).integers(0, n, 24))))

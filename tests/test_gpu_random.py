@@ -64,6 +64,23 @@ def _prompt_case(i, kv16):
                 seed=int(r.integers(0, 1 << 30)))
 
 
+def _own128_case(i, kv16):
+    # head_dim 128 row groups of 65..128 vectors: the own layout's eight compute waves
+    r = np.random.default_rng(5000 + i + (500 if kv16 else 0))
+    G = int(r.choice((4, 8, 16, 32, 64)))
+    hkv = int(r.choice((1, 2)))
+    rg = int(r.integers(65 // G + (65 % G > 0), 128 // G + 1))
+    rows = int(r.integers(rg, min(32, 3 * rg) + 1))
+    ctx = int(r.integers(0, 900))
+    tiles = (ctx + rows + 31) // 32
+    splits = int(r.integers(1, tiles + 1)) if r.random() < 0.5 else 0
+    qd = np.float32 if r.random() < 0.6 else np.float16
+    pad = int(r.integers(0, 40)) if r.random() < 0.5 else 0
+    peaked = 0.02 if r.random() < 0.3 else 0.0
+    return dict(hd=128, hq=G * hkv, hkv=hkv, rows=rows, ctx=ctx, rg=rg, splits=splits, qd=qd, pad=pad,
+                peaked=peaked, seed=int(r.integers(0, 1 << 30)))
+
+
 def _desc(c):
     return " ".join(f"{k}={v.__name__ if isinstance(v, type) else v}" for k, v in c.items())
 
@@ -131,3 +148,30 @@ def test_random_prompt_f16kv(i):
     note(f"  path: {ops.last_path()}")
     ref = oracle.prompt_f16kv(inp.q, inp.k, inp.v, c["pos0"])
     assert_parity(out.cpu().numpy(), ref, f"random prompt fp16 cache {i}")
+
+
+@pytest.mark.parametrize("kv16", [False, True], ids=["int8", "fp16"])
+@pytest.mark.parametrize("i", range(6))
+def test_random_verify_own128(i, kv16):
+    c = _own128_case(i, kv16)
+    note(f"random verify own layout hd128 {i} {'fp16' if kv16 else 'int8'} cache: {_desc(c)}")
+    w = W.VerifyWorkload("rand128", c["hq"], c["hkv"], c["hd"], c["ctx"], c["rows"], c["rg"],
+                         peaked_frac=c["peaked"], seed=c["seed"], kv_stride=c["ctx"] + c["rows"] + c["pad"])
+    if kv16:
+        inp = W.generate_f16kv(w)
+        inp.q = inp.q.astype(c["qd"])
+        ws, S = ops.verify_f16kv_partials(*_dev16(inp), ctx_len=c["ctx"], rows_per_group=c["rg"],
+                                          n_splits=c["splits"])
+        ref = oracle.verify_f16kv(inp.q, inp.k, inp.v, c["ctx"])
+    else:
+        inp = W.generate(w)
+        inp.q = inp.q.astype(c["qd"])
+        ws, S = ops.verify_partials(*to_device(inp), ctx_len=c["ctx"], rows_per_group=c["rg"],
+                                    n_splits=c["splits"])
+        ref = oracle.verify(inp.q, inp.k_codes, inp.k_scales, inp.v_codes, inp.v_scales, c["ctx"])
+    path = ops.last_path()  # the attention kernel's (the reducer records its own)
+    out = ops.reduce_partials(ws, c["rows"], c["hq"], c["hd"], S)
+    torch.cuda.synchronize()
+    note(f"  path: {path}")
+    assert "tiles8 own" in path
+    assert_parity(out.cpu().numpy(), ref, f"random verify own layout hd128 {i}")
