@@ -1,6 +1,7 @@
 // The int8-KV attention kernel shared by the verify and prompt paths.
 //
-// One workgroup of eight waves owns up to NQ x 16 query vectors (row, Q head)
+// One workgroup of eight waves (twelve for two or three vector tiles at head_dim
+// 256: body_waves) owns up to NQ x 16 query vectors (row, Q head)
 // of a group of consecutive rows that read one KV head -- the "one owner of
 // several query rows shares every K/V scan" organisation of "perf(gfx1100):
 // share Q8 KV scans across verifier rows" (Summary) -- and scans one range of
