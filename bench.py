@@ -112,13 +112,40 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def strip_comments(src: str) -> str:
+    """C++ source text without its comments, whitespace runs collapsed to one
+    space (string and character literals kept as they are)."""
+    out = []
+    i, n = 0, len(src)
+    while i < n:
+        c = src[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and src[j] != c:
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources: counter results are valid only for the sources they were taken on."""
+    """Hash of the HIP sources' code (comments and layout left out): counter
+    results are valid only for the code they were taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "attention_int8_quantized_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 

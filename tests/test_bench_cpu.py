@@ -34,6 +34,26 @@ def test_source_hash_is_stable_and_short():
     assert h == bench.kernel_source_hash() and len(h) == 16
 
 
+def test_source_hash_follows_code_not_comments(tmp_path, monkeypatch):
+    import shutil
+
+    csrc = tmp_path / "attention_int8_quantized_amd" / "csrc"
+    shutil.copytree(os.path.join(bench.ROOT, "attention_int8_quantized_amd", "csrc"), csrc)
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.kernel_source_hash()
+    f = csrc / "attend_kernel.h"
+    text = f.read_text()
+    f.write_text("// a new comment line\n" + text.replace("namespace attnq8 {", "namespace attnq8 {  /* x */", 1))
+    assert bench.kernel_source_hash() == h0
+    f.write_text(text.replace("kRescaleSlack = 15.0f", "kRescaleSlack = 14.0f", 1))
+    assert bench.kernel_source_hash() != h0
+
+
+def test_strip_comments_keeps_literals():
+    src = 'a = 1; // gone "x"\n/* gone\n */ s = "k // not /* a */ comment"; c = \'"\';'
+    assert bench.strip_comments(src) == 'a = 1; s = "k // not /* a */ comment"; c = \'"\';'
+
+
 def test_issued_mfma_flops_and_kernel_names():
     import workloads as W
 
