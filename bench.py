@@ -967,11 +967,24 @@ def time_head(ops, dev, steps, warmup, hold):
     path = ops.last_path()
     ev = timed_calls(call, steps, warmup, hold)
     t = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
+    # the same calls back to back (events around the region, divided by its
+    # launches): no per-call event latency
+    n_b2b = max(steps, 10)
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    hold(60e-6 * n_b2b + 1e-3)
+    r0.record()
+    for i in range(n_b2b):
+        call(i + 1, None)
+    r1.record()
+    torch.cuda.synchronize()
+    tb = r0.elapsed_time(r1) / n_b2b * 1e-3
     moved = rows * V * 4
     return {
         "workload": f"{rows} rows x {V} fp32 logits: greedy token + top probability",
         "path": path,
         "us_per_call": round(t * 1e6, 3),
+        "us_per_call_back_to_back": round(tb * 1e6, 3),
         "bytes": moved,
         "gbs": round(moved / t / 1e9, 1),
         "frac_hbm": round(moved / t / 1e9 / HBM_PEAK_GBS, 4),
