@@ -3,6 +3,8 @@
 // contract of every entry point.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <limits.h>
 #include <math.h>
 #include <mutex>
 #include <stdio.h>
@@ -24,6 +26,7 @@ constexpr int kTargetCUs = 256;           // MI355X compute units
 constexpr double kLog2e = 1.4426950408889634;
 constexpr int kMaxAppendHeadDim = 4096;   // KV append: any multiple of 32 up to this
 constexpr long long kAppendMaxBlocks = 8192;  // 32 workgroups per CU, then grid-stride
+constexpr int kMaxGridYZ = 65535;         // largest second and third grid dimension
 
 thread_local char g_last_path[192] = "none";
 
@@ -66,18 +69,21 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 bool head_dim_ok(int hd) { return hd == 64 || hd == 128 || hd == 256; }
 
-// Per-device architecture check, cached (0 = unknown, 1 = gfx950, 2 = other).
+// Per-device architecture check, cached (0 = unknown, 1 = gfx950, 2 = other;
+// atomic: threads that race on a device's first call store the same value).
 int device_status() {
-  static signed char cache[64] = {0};
+  static std::atomic<signed char> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return ATTNQ8_EHIP;
   if (dev < 0 || dev >= 64) return ATTNQ8_EUNSUPPORTED;
-  if (cache[dev] == 0) {
+  signed char c = cache[dev].load(std::memory_order_relaxed);
+  if (c == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTNQ8_EHIP;
-    cache[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    c = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    cache[dev].store(c, std::memory_order_relaxed);
   }
-  return cache[dev] == 1 ? ATTNQ8_OK : ATTNQ8_EUNSUPPORTED;
+  return c == 1 ? ATTNQ8_OK : ATTNQ8_EUNSUPPORTED;
 }
 
 int launch_status() {
@@ -206,6 +212,7 @@ int check_kv(const void* q, int q_dtype, const void* kc, const uint16_t* ks, con
   if (!KV16 && (!ks || !vs)) return ATTNQ8_EINVAL;
   if (q_dtype != ATTNQ8_F32 && q_dtype != ATTNQ8_F16) return ATTNQ8_EINVAL;
   if (hq <= 0 || hkv <= 0 || hq % hkv != 0) return ATTNQ8_EINVAL;
+  if (hkv > kMaxGridYZ) return ATTNQ8_EINVAL;  // the KV heads are the launch's third grid dimension
   if (!head_dim_ok(hd)) return ATTNQ8_EUNSUPPORTED;
   if (hq / hkv > kMaxVectorsPerGroup) return ATTNQ8_EUNSUPPORTED;
   if (kv_stride <= 0) return ATTNQ8_EINVAL;
@@ -400,6 +407,7 @@ int attn_reduce_partials(const void* workspace, size_t workspace_bytes, int n_ro
                          int head_dim, int n_splits, float* out, void* stream) {
   if (!workspace || !out) return ATTNQ8_EINVAL;
   if (n_rows < 1 || n_q_heads < 1 || n_splits < 1 || n_splits > 65535) return ATTNQ8_EINVAL;
+  if ((long long)n_rows * n_q_heads > INT_MAX) return ATTNQ8_EINVAL;  // (row, head) pairs: the grid's x
   if (!head_dim_ok(head_dim)) return ATTNQ8_EUNSUPPORTED;
   if (!aligned(workspace, 16) || !aligned(out, 16)) return ATTNQ8_EALIGN;
   if (workspace_bytes < attn_verify_q8_workspace_bytes(n_rows, n_q_heads, head_dim, n_splits))

@@ -81,7 +81,8 @@ enum { ATTNQ8_F32 = 0, ATTNQ8_F16 = 1 };
  * for a reference m near the largest x_t (not necessarily equal to it); a
  * split with no visible key holds m = -inf, l = 0, o = 0.
  *
- * Requirements: n_q_heads % n_kv_heads == 0; 1 <= n_rows <= 32;
+ * Requirements: n_q_heads % n_kv_heads == 0; n_kv_heads <= 65535 (also for
+ * the prompt and the fp16-cache calls); 1 <= n_rows <= 32;
  * ctx_len >= 0; ctx_len + n_rows <= kv_stride; q, codes and workspace 16-byte
  * aligned, scales 4-byte aligned; workspace_bytes >=
  * attn_verify_q8_workspace_bytes(n_rows, n_q_heads, head_dim, n_splits after
@@ -107,8 +108,9 @@ int attn_verify_q8(const void* q, int q_dtype,
  *     out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
  * in a fixed split order (run-to-run bitwise reproducible).  `workspace` holds
  * the layout above for the given n_splits; out is fp32
- * [n_rows][n_q_heads][head_dim], 16-byte aligned.  Every (row, head) must have
- * at least one split with l > 0.
+ * [n_rows][n_q_heads][head_dim], 16-byte aligned; n_rows * n_q_heads at most
+ * INT_MAX, 1 <= n_splits <= 65535.  Every (row, head) must have at least one
+ * split with l > 0.
  * ------------------------------------------------------------------------- */
 int attn_reduce_partials(const void* workspace, size_t workspace_bytes,
                          int n_rows, int n_q_heads, int head_dim, int n_splits,

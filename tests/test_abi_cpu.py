@@ -95,6 +95,7 @@ def _verify(lib, **kw):
     (dict(ws=A + 4), _lib.EALIGN),
     (dict(ws_bytes=100), _lib.EWORKSPACE),
     (dict(splits=9, ws_bytes=9 * 4 * 4 * 66 * 4 - 1), _lib.EWORKSPACE),
+    (dict(hq=65536, hkv=65536), _lib.EINVAL),  # KV heads beyond the launch's third grid dimension
 ])
 def test_verify_rejects_before_launch(lib, kw, status):
     assert _verify(lib, **kw) == status
@@ -122,6 +123,7 @@ def _prompt(lib, **kw):
     (dict(out=A + 4), _lib.EALIGN),
     (dict(vc=A + 1), _lib.EALIGN),
     (dict(sm=float("nan")), _lib.EINVAL),
+    (dict(hq=65536, hkv=65536), _lib.EINVAL),  # KV heads beyond the launch's third grid dimension
 ])
 def test_prompt_rejects_before_launch(lib, kw, status):
     assert _prompt(lib, **kw) == status
@@ -136,6 +138,8 @@ def test_reduce_rejects_before_launch(lib):
     assert f(A, 1 << 20, 4, 4, 48, 2, A, None) == _lib.EUNSUPPORTED
     assert f(A + 4, 1 << 20, 4, 4, 64, 2, A, None) == _lib.EALIGN
     assert f(A, 100, 4, 4, 64, 2, A, None) == _lib.EWORKSPACE
+    # (row, head) pairs past INT_MAX would wrap the grid size
+    assert f(A, 1 << 62, 1 << 16, 1 << 15, 64, 1, A, None) == _lib.EINVAL
 
 
 def _append(lib, **kw):
