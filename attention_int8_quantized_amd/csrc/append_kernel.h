@@ -8,9 +8,17 @@
 //   scale = fp16_rne(amax / 127)              (fp32 divide, then fp16)
 //   code  = clamp(round_half_away(x / scale), -127, 127)   (fp32 divide)
 //   scale == 0  ->  every code 0
-// Both divides are IEEE fp32 divides (HIP's default division is correctly
-// rounded); neither can land on a rounding boundary it did not reach exactly,
-// so the result equals the exactly rounded one.
+// The scale's divide is an IEEE fp32 divide (HIP's default division is
+// correctly rounded).  The code's fp32 quotient never lands on a rounding
+// boundary it did not reach exactly (an fp16 scale times k + 1/2 has at most 19
+// significant bits, so any other fp32 x lies at least one of its ulps away), so
+// the code is the exactly rounded |x| / scale: it is taken as
+// k = floor(|x| * rcp(scale)) -- within 3e-5 of |x| / scale, so k is the floor
+// of the exact quotient or one off across an integer -- plus 1 when
+// |x| - (k + 1/2) * scale >= 0, a difference one fma computes with the exact
+// sign ((k + 1/2) * scale is exact in fp32; equality is the tie, which goes
+// away from zero); then the clamp and x's sign.  This replaces eight divides
+// per lane with a reciprocal and a few multiply-adds.
 //
 // Mapping: a lane owns 8 consecutive elements (one 32-byte or 16-byte load), a
 // quad of lanes owns a block; the block maximum is two DPP quad permutes.  The
@@ -95,13 +103,19 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_q8_kernel(AppendArgs
     const float amax = __uint_as_float(quad_max_u32(m));
     const __half s16 = __float2half_rn(amax / 127.0f);
     const float d = __half2float(s16);
+    // a zero scale (an all-zero block) and an infinite one (a block beyond
+    // fp16's range) both give code 0: with the divisor taken as +inf the
+    // reciprocal is 0 and the rounding test below never passes
+    const float dv = d == 0.0f ? __builtin_inff() : d;
+    const float rinv = __builtin_amdgcn_rcpf(dv);  // v_rcp_f32, about 1 ulp
 
     float y[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      float r = roundf(x[i] / d);
-      r = fminf(fmaxf(r, -127.0f), 127.0f);
-      y[i] = d == 0.0f ? 0.0f : r;
+      const float ax = fabsf(x[i]);
+      float k = floorf(ax * rinv);
+      k = fmaf(-(k + 0.5f), dv, ax) >= 0.0f ? k + 1.0f : k;  // |x| >= (k + 1/2) scale, exactly
+      y[i] = __builtin_copysignf(fminf(k, 127.0f), x[i]);
     }
 
     const int h = in_row / a.head_units;
