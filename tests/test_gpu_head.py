@@ -42,7 +42,8 @@ def _run(x, ws=None):
 
 
 @pytest.mark.parametrize("rows,vocab", [(1, 248320), (4, 248320), (5, 248320), (8, 248320),
-                                        (3, 106299), (2, 1), (3, 7), (1, 2049), (64, 4096)])
+                                        (3, 106299), (2, 1), (3, 7), (1, 2049), (64, 4096),
+                                        (257, 1000), (1024, 3000)])  # one block per row
 def test_head_matches_oracle(rows, vocab):
     note(f"verify head rows={rows} vocab={vocab}")
     rng = np.random.default_rng(rows * 1000 + vocab % 997)

@@ -42,6 +42,8 @@ SMALL = [
     (1, 1, 128, 500, 100, 400, 0, np.float16),
     (6, 2, 256, 129, 40, 80, 0, np.float32),
     (16, 1, 64, 2000, 96, None, 0, np.float16),
+    (128, 1, 256, 300, 20, None, 0, np.float16),   # 128 vectors per query at head_dim 256
+    (128, 2, 64, 150, 9, 3, 0, np.float32),        # 128 vectors per query at head_dim 64
 ]
 
 

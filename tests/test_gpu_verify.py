@@ -81,6 +81,8 @@ SMALL = [
     (24, 4, 256, 777, 32, 0, 0, np.float16, 0),
     (24, 2, 256, 900, 8, 8, 0, np.float32, 0),    # 96 vectors per group: the own layout
     (24, 2, 256, 333, 13, 8, 3, np.float16, 2),   # own layout; groups of 8 and 5 rows
+    (128, 1, 256, 100, 1, 0, 0, np.float32, 0),   # 128 vectors at head_dim 256: the eight-tile body
+    (128, 2, 256, 150, 2, 1, 2, np.float16, 1),   # the same, two KV heads, two groups of one row
 ]
 
 
